@@ -1,0 +1,415 @@
+// sa_attn.hip -- gathered sparse attention with per-head sinks, bf16 storage, for gfx950.
+//
+// What it computes: akol1/TensorFold pull request 4 ("DeepSeek V4.1: sparse
+// attention on eight SIMD groups, the same bytes"), first commit message: for a
+// query row and its heads, the selected keys are scored in 64-key tiles against a
+// 512-wide head (sixteen 32-wide output column groups), with a running maximum, a
+// tile sum and a value sum kept in a fixed order. TensorFold pull request 1206,
+// "What changes": every head has a sink logit (zero for padded heads).
+//
+// How it maps to CDNA4 (this is not the pages' one-SIMD-group-per-head design):
+//   * One workgroup serves one query row and a block of 32 or 64 heads, because
+//     the key/value latent is shared by all heads of a row: each selected cache
+//     row is gathered from HBM once per row, not once per head.
+//   * The gather is an index-driven direct-to-LDS DMA (global_load_lds_dwordx4):
+//     one wave instruction moves one whole 1 KiB cache row (or the workgroup's
+//     column slice of it), so every gather is a fully coalesced burst. K and V tiles sit in two LDS buffers; the next
+//     tile's K is in flight while the current tile's values are applied, and the
+//     next tile's V while the next scores are formed.
+//   * S^T = K Q^T and O^T = V^T P^T run on v_mfma_f32_32x32x16_bf16 with the heads
+//     on the N side, so every lane owns one head: the row maximum and the tile sum
+//     are an in-lane reduction over 16 scores plus one exchange with lane^32, and
+//     the two waves that split a tile's 64 keys combine their halves in LDS in a
+//     fixed order. V^T operands come from ds_read_b64_tr_b16 transposing reads.
+//   * Splitting work across workgroups only ever splits heads and output columns,
+//     never keys, so each (row, head, column) is produced by the same sequence of
+//     operations whatever the batch size or head count: results are bit-identical
+//     across launch shapes and repeats, and no workspace or combine pass exists.
+//
+// Numerics (the fixed order): per 64-key tile, m' = max(m, max_j s_j); the
+// reference r = m' unless m' = -inf, then 0; alpha = exp(m - r); p_j = exp(s_j - r)
+// rounded to bf16; l = alpha*l + sum_j p_j (the same rounded p); acc = alpha*acc +
+// P V; m = m'. Start: m = sink, l = exp(sink - r(sink)), acc = 0. End: acc / l.
+// Keys past a row's count score -inf by select and gather a zero row, so a tail
+// tile never multiplies a stale LDS value.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "sa_internal.h"
+
+namespace sa {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+#define SA_LDS __attribute__((address_space(3)))
+
+constexpr int kHeadDim = 512;   // sixteen 32-wide output column groups
+constexpr int kTile = 64;       // keys per online-softmax tile
+constexpr int kRowBytes = kHeadDim * 2;
+
+// Source of the DMA for keys that are masked or invalid: 1 KiB of zeros.
+__device__ __attribute__((aligned(16))) const uint32_t g_zero_row[kRowBytes / 4] = {0};
+
+// All vector-memory traffic inside the tile loop is issued through the asm helpers
+// below, so the compiler neither sees nor waits on it: the loop's only waits on the
+// vector-memory counter are the explicit ones, each placed where one tile's
+// gathers must have landed while the next tile's stay in flight.
+
+// s_waitcnt vmcnt(N): this wave has at most N vector-memory operations outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Workgroup barrier for LDS traffic only: outstanding LDS operations complete,
+// in-flight DMA gathers stay in flight.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+    return (uint32_t)(uintptr_t)(const SA_LDS void *)p;
+}
+
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+// Direct-to-LDS gather: lane i moves 16 bytes from sbase + voff_i to LDS address
+// lds + 16 i (M0 holds the wave's LDS base). sbase and lds are wave-uniform.
+__device__ __forceinline__ void dma16(const void *sbase, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 ::"s"(lds), "v"(voff), "s"(sbase) : "memory", "m0");
+}
+// Same with 4 bytes per lane (LDS address lds + 4 i).
+__device__ __forceinline__ void dma4(const void *sbase, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
+                 ::"s"(lds), "v"(voff), "s"(sbase) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Bits 2 and 3 of m exchanged. Row m of a 32-key MFMA block holds key pi(m), which
+// makes each lane's sixteen scores two runs of eight consecutive keys (the P operand).
+__device__ __forceinline__ int swap23(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
+
+// LDS row strides. A K row is padded by 16 bytes: the 16 lanes of one ds_read_b128
+// read 16 consecutive slots at the same column and land on 16 different 16-byte
+// bank groups. A V row is padded by 64 bytes: one ds_read_b64_tr_b16 reads rows
+// {0..3} + 8g of a 16-key step at a 64-byte column window, and with a stride of
+// 64 (mod 256) bytes every 4-byte bank is hit exactly twice by its 512 bytes.
+// Either way each read is one base register plus an immediate offset.
+constexpr int kKStride = kRowBytes + 16;
+
+// K slot s holds tile key (s & 32) | swap23(s & 31), so MFMA row m of key block kb
+// (which must hold key kb*32 + swap23(m)) reads slot kb*32 + m.
+__device__ __forceinline__ int key_of_slot(int s) { return (s & 32) | swap23(s & 31); }
+
+// Map the linear workgroup id so that the workgroups of one query row (its head
+// groups and column slices, which gather the same cache rows) run on one XCD and
+// share its L2. Dispatch places workgroup i on XCD i % 8.
+__device__ __forceinline__ int64_t xcd_remap(int64_t i, int64_t G) {
+    const int64_t xcd = i & 7, slot = i >> 3;
+    const int64_t per = G >> 3, rem = G & 7;
+    return xcd * per + (xcd < rem ? xcd : rem) + slot;
+}
+
+// Kernel template.
+//   HB: head blocks of 32 per workgroup (1 or 2); the workgroup has 2*HB waves.
+//   NT: 32-column output groups per wave; the workgroup covers 64*NT columns.
+// Wave w: head block hb = w/2; key half kb = w%2 of each tile for the scores; the
+// same kb picks which half of the workgroup's columns the wave accumulates.
+template <int HB, int NT>
+__global__ void __launch_bounds__(128 * HB) __attribute__((amdgpu_waves_per_eu(1, 1)))
+attn_bf16_kernel(AttnArgs a, int n_hg) {
+    constexpr int WAVES = 2 * HB;
+    constexpr int COLS = 64 * NT;              // output columns per workgroup
+    constexpr int VROW = COLS * 2;             // bytes of one V row slice
+    constexpr int VSTRIDE = VROW + 64;         // padded V row stride in LDS
+    constexpr int VCHUNKS = VROW / 16;         // 16-byte pieces of a V row slice
+    constexpr int NK = kTile / WAVES;          // K rows gathered per wave per tile
+    constexpr int NV = kTile / WAVES;          // V rows gathered per wave per tile
+    constexpr int N_CS = kHeadDim / COLS;
+    static_assert(NK * WAVES == kTile, "tile split");
+    static_assert(NV + 1 < 64 && NK < 64, "vmcnt range");
+
+    __shared__ __attribute__((aligned(16))) char k_lds[kTile * kKStride];
+    __shared__ __attribute__((aligned(16))) char v_lds[kTile * VSTRIDE];
+    __shared__ __attribute__((aligned(16))) bf16x8 p_lds[WAVES][2][64];
+    __shared__ float max_lds[WAVES][32];
+    __shared__ float sum_lds[WAVES][32];
+    __shared__ int idx_lds[WAVES][2][64];   // each wave's own copy of a tile's index list
+
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int g = lane >> 5;
+    const int ln = lane & 31;
+    const int hb = w >> 1;
+    const int kb = w & 1;
+
+    const int64_t G = (int64_t)gridDim.x;
+    const int64_t lid = xcd_remap(blockIdx.x, G);
+    const int cs = (int)(lid % N_CS);
+    const int hg = (int)((lid / N_CS) % n_hg);
+    const int64_t row = lid / ((int64_t)N_CS * n_hg);
+
+    const int head = (hg * HB + hb) * 32 + ln;
+    const bool head_ok = head < a.H;
+    const int col0 = cs * COLS + kb * NT * 32;        // first output column of this wave
+
+    // Heads past H (internal padding to the 32-head block) read head 0 and are zeroed.
+    const uint16_t *qrow = (const uint16_t *)a.q + ((int64_t)row * a.H + (head_ok ? head : 0)) * kHeadDim;
+    const bf16x8 qmask_zero = (bf16x8){};
+    const char *kbase = (const char *)a.k + (int64_t)row * a.cache_stride * 2;
+    const char *vbase = (const char *)a.v + (int64_t)row * a.cache_stride * 2 + (int64_t)cs * VROW;
+    const int32_t *irow = a.idx + (int64_t)row * a.kmax;
+    int n = a.nsel ? a.nsel[row] : a.kmax;
+    n = n < 0 ? 0 : (n > a.kmax ? a.kmax : n);
+    const int ntiles = (n + kTile - 1) / kTile;
+
+    // Query operand of S^T = K Q^T: lane (head ln, half g) holds d = 256g + 8kk + 0..7.
+    bf16x8 qreg[32];
+#pragma unroll
+    for (int kk = 0; kk < 32; kk++) {
+        const bf16x8 v = *(const bf16x8 *)(qrow + 256 * g + 8 * kk);
+        qreg[kk] = head_ok ? v : qmask_zero;
+    }
+
+    // Index list of tile t into this wave's slot buf: lane l fetches entry t*64 + l
+    // (address clamped to the row, so the fetch is always issued: every wave then
+    // issues the same number of vector-memory operations per tile).
+    auto dma_idx = [&](int t, int buf) {
+        const int p = t * kTile + lane;
+        const int pc = p < a.kmax ? p : a.kmax - 1;
+        dma4(irow, (uint32_t)pc * 4u, lds_addr(&idx_lds[w][buf][0]));
+    };
+    // Row to gather for entry t*64 + l, or -1 (masked or out of range: gather zeros).
+    auto resolve = [&](int t, int buf, bool &bad) -> int {
+        const int iv = idx_lds[w][buf][lane];
+        const int p = t * kTile + lane;
+        const bool live = p < n;
+        const bool inr = iv >= 0 && (int64_t)iv < a.n_ctx;
+        if (__builtin_amdgcn_ballot_w64(live && !inr)) bad = true;
+        return (live && inr) ? iv : -1;
+    };
+
+    // One DMA instruction gathers one cache row (64 lanes x 16 bytes = 1 KiB) into
+    // an LDS slot; lane i moves bytes [16i, 16i + 16) of the row.
+    auto dma_k = [&](int iv) {
+#pragma unroll
+        for (int i = 0; i < NK; i++) {
+            const int slot = w * NK + i;
+            const int ij = __builtin_amdgcn_readlane(iv, key_of_slot(slot));
+            const char *rbase = ij >= 0 ? kbase + (int64_t)ij * kRowBytes : (const char *)g_zero_row;
+            dma16(rbase, (uint32_t)lane << 4, lds_addr(k_lds + slot * kKStride));
+        }
+    };
+    // V rows keep the tile's key order; only this workgroup's column slice is moved.
+    auto dma_v = [&](int iv) {
+#pragma unroll
+        for (int i = 0; i < NV; i++) {
+            const int j = w * NV + i;
+            const int ij = __builtin_amdgcn_readlane(iv, j);
+            const char *rbase = ij >= 0 ? vbase + (int64_t)ij * kRowBytes : (const char *)g_zero_row;
+            if (VCHUNKS == 64 || lane < VCHUNKS) dma16(rbase, (uint32_t)lane << 4, lds_addr(v_lds + j * VSTRIDE));
+        }
+    };
+
+    const float sink = head_ok ? a.sinks[head] : 0.0f;
+    float m_run = sink;
+    const float r0 = (sink == -INFINITY) ? 0.0f : sink;
+    float l_run = expf(sink - r0);
+    f32x16 acc[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; nt++) acc[nt] = (f32x16){};
+    bool bad = false;
+
+    // The query and sink loads above are the compiler's own; let them complete here
+    // so that nothing the compiler tracks is pending inside the loop.
+    __builtin_amdgcn_s_waitcnt(0);
+
+    if (ntiles > 0) {
+        // Issue order per wave: K(0), I(1), V(0); then in iteration t: K(t+1) after the
+        // scores, I(t+2) and V(t+1) after the values.
+        dma_idx(0, 0);
+        wait_vmcnt<0>();
+        const int iv0 = resolve(0, 0, bad);
+        dma_k(iv0);
+        dma_idx(1, 1);
+        dma_v(iv0);
+
+        for (int t = 0; t < ntiles; t++) {
+            const bool more = t + 1 < ntiles;
+            // K(t) has landed for this wave (I(t+1) and V(t) may be in flight).
+            wait_vmcnt<NV + 1>();
+            lds_barrier();
+
+            // ---- scores S^T (32 keys of half kb) x (32 heads), K from LDS, Q in registers.
+            f32x16 sacc = (f32x16){};
+            {
+                const SA_LDS char *krow = (const SA_LDS char *)k_lds + (kb * 32 + ln) * kKStride + 512 * g;
+#pragma unroll
+                for (int kk = 0; kk < 32; kk++) {
+                    const bf16x8 kop = *(const SA_LDS bf16x8 *)(krow + 16 * kk);
+                    sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qreg[kk], sacc, 0, 0, 0);
+                    if ((kk & 7) == 7) __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+            // Element e of this lane is key kb*32 + 16*(e/8) + 8g + e%8 of the tile.
+            float s[16];
+            float mloc = -INFINITY;
+#pragma unroll
+            for (int e = 0; e < 16; e++) {
+                const int p = t * kTile + kb * 32 + 16 * (e >> 3) + 8 * g + (e & 7);
+                s[e] = p < n ? sacc[e] * a.scale : -INFINITY;
+                mloc = fmaxf(mloc, s[e]);
+            }
+            mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+            if (g == 0) max_lds[w][ln] = mloc;
+            lds_barrier();  // every wave is also done reading k_lds
+
+            // Indices of tile t+1 have landed; start gathering its K.
+            wait_vmcnt<NV>();
+            int iv_n = 0;
+            if (more) {
+                iv_n = resolve(t + 1, (t + 1) & 1, bad);
+                dma_k(iv_n);
+            }
+
+            // ---- online softmax with the sink, fixed order.
+            const float mt = fmaxf(max_lds[2 * hb][ln], max_lds[2 * hb + 1][ln]);
+            const float m_new = fmaxf(m_run, mt);
+            const float ref = (m_new == -INFINITY) ? 0.0f : m_new;
+            const float alpha = expf(m_run - ref);
+            bf16x8 pk0, pk1;
+            float psum = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 16; e++) {
+                const __bf16 pb = (__bf16)expf(s[e] - ref);
+                psum += (float)pb;
+                if (e < 8) pk0[e] = pb; else pk1[e - 8] = pb;
+            }
+            psum += __shfl_xor(psum, 32);
+            p_lds[w][0][lane] = pk0;
+            p_lds[w][1][lane] = pk1;
+            if (g == 0) sum_lds[w][ln] = psum;
+
+            // V(t) has landed (K(t+1) may be in flight).
+            if (more) wait_vmcnt<NK>(); else wait_vmcnt<0>();
+            lds_barrier();
+
+            l_run = alpha * l_run + (sum_lds[2 * hb][ln] + sum_lds[2 * hb + 1][ln]);
+            m_run = m_new;
+
+            // ---- values O^T += V^T P^T over the tile's four 16-key steps.
+            bf16x8 pop[4];
+#pragma unroll
+            for (int ks = 0; ks < 4; ks++) pop[ks] = p_lds[2 * hb + (ks >> 1)][ks & 1][lane];
+            // Lane (g, ch, l16) addresses row 16ks + 8g + 4t2 + l16/4 and columns
+            // 32nt + 16ch + 4(l16%4) .. +3 of the wave's half of the slice; the
+            // transposing read returns column 32nt + 16ch + l16 of rows +0..3.
+            const int l16 = lane & 15;
+            const int ch = (lane >> 4) & 1;
+            const SA_LDS char *vrow = (const SA_LDS char *)v_lds + (8 * g + (l16 >> 2)) * VSTRIDE +
+                                      2 * (kb * NT * 32 + 16 * ch + 4 * (l16 & 3));
+#pragma unroll
+            for (int nt = 0; nt < NT; nt++) {
+                acc[nt] *= alpha;
+#pragma unroll
+                for (int ks = 0; ks < 4; ks++) {
+                    bf16x8 vop;
+#pragma unroll
+                    for (int t2 = 0; t2 < 2; t2++) {
+                        const bf16x4 part = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                            (SA_LDS bf16x4 *)(vrow + (16 * ks + 4 * t2) * VSTRIDE + 64 * nt));
+                        vop[4 * t2 + 0] = part[0];
+                        vop[4 * t2 + 1] = part[1];
+                        vop[4 * t2 + 2] = part[2];
+                        vop[4 * t2 + 3] = part[3];
+                    }
+                    acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pop[ks], acc[nt], 0, 0, 0);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            lds_barrier();  // every wave is done with v_lds and p_lds
+
+            dma_idx(t + 2, t & 1);  // slot t&1 held tile t's list, consumed above
+            if (more) dma_v(iv_n);
+        }
+        wait_vmcnt<0>();
+    }
+
+    // ---- normalise and store: lane holds head ln, columns col0 + 32nt + 8(e/4) + 4g + e%4.
+    if (head_ok) {
+        float *orow = a.out + ((int64_t)row * a.H + head) * kHeadDim;
+        const float inv_nan = bad ? NAN : 0.0f;
+#pragma unroll
+        for (int nt = 0; nt < NT; nt++) {
+#pragma unroll
+            for (int eq = 0; eq < 4; eq++) {
+                f32x4 o;
+#pragma unroll
+                for (int i = 0; i < 4; i++) o[i] = bad ? inv_nan : acc[nt][4 * eq + i] / l_run;
+                *(f32x4 *)(orow + col0 + 32 * nt + 8 * eq + 4 * g) = o;
+            }
+        }
+    }
+}
+
+template <int HB, int NT>
+hipError_t launch_variant(const AttnArgs &a, int64_t grid, hipStream_t s) {
+    const int n_hg = (a.H + 32 * HB - 1) / (32 * HB);
+    hipLaunchKernelGGL((attn_bf16_kernel<HB, NT>), dim3((unsigned)grid), dim3(128 * HB), 0, s, a, n_hg);
+    return hipGetLastError();
+}
+
+constexpr int lds_bytes_of(int HB, int NT) {
+    return kTile * kKStride + kTile * (128 * NT + 64) + 2 * HB * 2 * 64 * 16 + 2 * 2 * HB * 32 * 4;
+}
+
+}  // namespace
+
+AttnPlan plan_attn_bf16(int64_t rows, int H) {
+    AttnPlan p{};
+    const int hb = H > 32 ? 2 : 1;
+    p.heads_per_wg = 32 * hb;
+    const int64_t n_hg = (H + p.heads_per_wg - 1) / p.heads_per_wg;
+    const int64_t units = rows * n_hg;
+    // One workgroup per CU fits (the K tile alone is 64 KiB of LDS). With fewer
+    // (row, head block) units than CUs, column slices add workgroups; every slice
+    // gathers the full K tile but only its own V columns.
+    int nt = 8;
+    if (units < 64) nt = 1;
+    else if (units < 128) nt = 2;
+    else if (units < 256) nt = 4;
+    p.cols_per_wg = 64 * nt;
+    p.grid = units * (kHeadDim / p.cols_per_wg);
+    p.threads = 128 * hb;
+    p.lds_bytes = lds_bytes_of(hb, nt);
+    return p;
+}
+
+hipError_t launch_attn_bf16(const AttnArgs &a, hipStream_t s) {
+    const AttnPlan p = plan_attn_bf16(a.rows, a.H);
+    if (p.grid == 0) return hipSuccess;
+    const int nt = p.cols_per_wg / 64;
+    if (p.heads_per_wg == 64) {
+        switch (nt) {
+            case 1: return launch_variant<2, 1>(a, p.grid, s);
+            case 2: return launch_variant<2, 2>(a, p.grid, s);
+            case 4: return launch_variant<2, 4>(a, p.grid, s);
+            default: return launch_variant<2, 8>(a, p.grid, s);
+        }
+    }
+    switch (nt) {
+        case 1: return launch_variant<1, 1>(a, p.grid, s);
+        case 2: return launch_variant<1, 2>(a, p.grid, s);
+        case 4: return launch_variant<1, 4>(a, p.grid, s);
+        default: return launch_variant<1, 8>(a, p.grid, s);
+    }
+}
+
+}  // namespace sa

@@ -1,0 +1,115 @@
+"""The C-ABI library loads without a GPU, exports every declared symbol, and rejects
+invalid arguments on the host before anything is enqueued (no compute calls here)."""
+import os
+import re
+
+import pytest
+
+from sparse_attention_attn_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sparse_attn.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(L.LIB_PATH), reason="libsparse_attn.so not built")
+
+A16 = 0x10000  # fake, 16-byte aligned device addresses: never dereferenced by these calls
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(sparse_attn_\w+)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    assert declared_symbols() == sorted(L.SIGNATURES)
+
+
+def test_every_declared_symbol_is_exported():
+    lib = L.load()
+    for name in declared_symbols():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings():
+    lib = L.load()
+    assert lib.sparse_attn_abi_version() == 1
+    for code in range(6):
+        assert lib.sparse_attn_status_string(code)
+    assert lib.sparse_attn_status_string(99) == b"unknown status"
+    assert lib.sparse_attn_workspace_bytes(L.SA_OP_DECODE, 1024, 64, 512, 640, 4096) == 0
+
+
+def _decode(lib, **kw):
+    args = dict(dtype=L.SA_BF16, q=A16, k=A16, v=A16, n_ctx=4096, idx=A16, nsel=None, kmax=640, sinks=A16,
+                scale=0.044, rows=8, H=64, D=512, out=A16, ws=None, ws_bytes=0, stream=None)
+    args.update(kw)
+    return lib.sparse_attn_decode(*args.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), L.SA_ERR_NULL),
+    (dict(k=None), L.SA_ERR_NULL),
+    (dict(out=None), L.SA_ERR_NULL),
+    (dict(sinks=None), L.SA_ERR_NULL),
+    (dict(idx=None), L.SA_ERR_NULL),
+    (dict(D=256), L.SA_ERR_UNSUPPORTED),
+    (dict(dtype=7), L.SA_ERR_UNSUPPORTED),
+    (dict(H=0), L.SA_ERR_SHAPE),
+    (dict(H=129), L.SA_ERR_SHAPE),
+    (dict(rows=-1), L.SA_ERR_SHAPE),
+    (dict(kmax=0), L.SA_ERR_SHAPE),
+    (dict(n_ctx=0), L.SA_ERR_SHAPE),
+    (dict(q=A16 + 8), L.SA_ERR_UNSUPPORTED),
+    (dict(out=A16 + 4), L.SA_ERR_UNSUPPORTED),
+    (dict(idx=A16 + 2), L.SA_ERR_UNSUPPORTED),
+])
+def test_decode_validation(kw, code):
+    lib = L.load()
+    assert _decode(lib, **kw) == code
+    assert lib.sparse_attn_last_error()  # a message names the problem
+
+
+def test_prefill_validation():
+    lib = L.load()
+    args = [L.SA_BF16, A16, A16, A16, 4096, A16, None, 640, A16, 0.04, 2048, 64, 512, A16, None, 0, None]
+    bad = list(args); bad[12] = 128
+    assert lib.sparse_attn_prefill(*bad) == L.SA_ERR_UNSUPPORTED
+    bad = list(args); bad[1] = None
+    assert lib.sparse_attn_prefill(*bad) == L.SA_ERR_NULL
+
+
+def test_topk_validation():
+    lib = L.load()
+    ok = [A16, 8, 32768, 32768, None, 640, A16, A16, None, 0, None]
+    for i, val, code in [(0, None, L.SA_ERR_NULL), (6, None, L.SA_ERR_NULL), (5, 0, L.SA_ERR_SHAPE),
+                         (3, 100, L.SA_ERR_SHAPE), (1, -1, L.SA_ERR_SHAPE), (2, -5, L.SA_ERR_SHAPE),
+                         (0, A16 + 2, L.SA_ERR_UNSUPPORTED)]:
+        bad = list(ok); bad[i] = val
+        assert lib.sparse_attn_topk(*bad) == code, (i, val)
+
+
+def test_pad_validation():
+    lib = L.load()
+    assert lib.sparse_attn_pad_heads(L.SA_BF16, A16, 10, 16, 8, 512, A16, A16, A16, None) == L.SA_ERR_SHAPE
+    assert lib.sparse_attn_pad_heads(L.SA_BF16, A16, 10, 16, 32, 500, A16, A16, A16, None) == L.SA_ERR_UNSUPPORTED
+    assert lib.sparse_attn_pad_heads(L.SA_BF16, None, 10, 16, 32, 512, A16, A16, A16, None) == L.SA_ERR_NULL
+    assert lib.sparse_attn_unpad_heads(A16, 10, 32, 33, 512, A16, None) == L.SA_ERR_SHAPE
+    assert lib.sparse_attn_unpad_heads(A16, 10, 32, 16, 512, None, None) == L.SA_ERR_NULL
+
+
+def test_python_binding_refuses_cpu_tensors():
+    import torch
+    import sparse_attention_attn_amd as sa
+    q = torch.zeros(1, 4, 512, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        sa.decode(q, torch.zeros(1, 8, 512, dtype=torch.bfloat16), torch.zeros(1, 8, 512, dtype=torch.bfloat16),
+                  torch.zeros(1, 4, dtype=torch.int32), torch.zeros(4), 0.04)
+
+
+def test_zero_rows_is_a_noop_with_null_arrays():
+    lib = L.load()
+    assert _decode(lib, q=None, k=None, v=None, idx=None, out=None, rows=0) == L.SA_OK
+    assert lib.sparse_attn_prefill(L.SA_BF16, None, A16, A16, 10, None, None, 4, A16, 0.1, 0, 64, 512,
+                                   None, None, 0, None) == L.SA_OK
+    assert lib.sparse_attn_topk(None, 0, 100, 100, None, 10, None, None, None, 0, None) == L.SA_OK
+    assert _decode(lib, rows=0, D=256) == L.SA_ERR_UNSUPPORTED  # sizes are still checked

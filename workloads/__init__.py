@@ -217,3 +217,44 @@ def indexer_then_decode(seed: int = 4, batch: int = 8, heads: int = 64, n_ctx: i
 
 
 EDGE_K = (1, 63, 64, 65, 639, 641)
+
+
+def device_decode_inputs(torch, device, batch: int, heads: int, n_ctx: int, k: int, seed: int,
+                         chunk_rows: int = 32):
+    """Decode inputs generated on the device with a seeded torch generator.
+
+    For shapes too large to draw on the host (1,024 sequences x 4,096 positions
+    x 512 is 4 GiB per cache in bf16). Values are N(0,1) float32 draws rounded
+    to bf16; each row's k indices are distinct and uniform over the cache
+    (the first k of a random permutation), sorted ascending.
+    """
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    f32, bf = torch.float32, torch.bfloat16
+    q = torch.randn((batch, heads, D), generator=g, device=device, dtype=f32).to(bf)
+    kc = torch.empty((batch, n_ctx, D), dtype=bf, device=device)
+    vc = torch.empty((batch, n_ctx, D), dtype=bf, device=device)
+    for cache in (kc, vc):
+        for b0 in range(0, batch, chunk_rows):
+            b1 = min(batch, b0 + chunk_rows)
+            cache[b0:b1] = torch.randn((b1 - b0, n_ctx, D), generator=g, device=device, dtype=f32).to(bf)
+    sinks = torch.randn((heads,), generator=g, device=device, dtype=f32)
+    perm = torch.rand((batch, n_ctx), generator=g, device=device).argsort(dim=1)[:, :k]
+    idx = perm.sort(dim=1).values.to(torch.int32).contiguous()
+    return {"q": q, "k": kc, "v": vc, "idx": idx, "sinks": sinks, "nsel": None}
+
+
+def host_case_from_device(inp, row: int, name: str = "device_row") -> AttnCase:
+    """Copy one row of device decode inputs (its query, its cache, its indices) to the host."""
+    import torch
+
+    def bits(t):
+        return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+    q = bits(inp["q"][row:row + 1])
+    kc = bits(inp["k"][row:row + 1])
+    vc = bits(inp["v"][row:row + 1])
+    idx = inp["idx"][row:row + 1].cpu().numpy().astype(np.int32)
+    sinks = inp["sinks"].cpu().numpy().astype(np.float32)
+    nsel = np.full(1, idx.shape[1], np.int32)
+    return AttnCase(name, "bf16", q, kc, vc, idx, nsel, sinks, SCALE, False)
