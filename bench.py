@@ -21,7 +21,6 @@ from __future__ import annotations
 
 import argparse
 import json
-import math
 import os
 import sys
 import time
@@ -48,32 +47,46 @@ def algorithmic_flops(rows: int, heads: int, d: int, k: int) -> int:
     return rows * 4 * heads * d * k
 
 
-def cpu_baseline(inp, scores, heads, k, budget_s: float, max_rows: int):
-    """Time the float64 oracle (top-k then attention) on the host on a bounded sample of rows."""
+def cpu_baseline(inp, scores, out_gpu, idx_gpu, heads, k, budget_s: float, max_rows: int):
+    """Time the float64 oracle (top-k then attention) on the host on a bounded sample of rows.
+
+    The oracle's results for those rows are also compared with what the timed GPU
+    launch produced for them (indices bit-exact; attention within the bf16 tolerance
+    |g - o| <= 2e-3 + 1e-2 |o| with equal nonfinite classes)."""
     import numpy as np
 
     import oracle
     import workloads as w
     threads = len(os.sched_getaffinity(0))
     lib = oracle.load()
-    rows_done = 0
-    t_total = 0.0
-    r = 0
-    while r < max_rows and t_total < budget_s:
+    rows_done, t_total, max_err, ok = 0, 0.0, 0.0, True
+    out_host = out_gpu.cpu().numpy()
+    idx_host = idx_gpu.cpu().numpy()
+    while rows_done < max_rows and t_total < budget_s:
+        r = rows_done
         case = w.host_case_from_device(inp, r)
         s = scores[r:r + 1].cpu().numpy()
         t0 = time.perf_counter()
         idx, cnt = oracle.topk(s, k, lib=lib)
         case.idx, case.nsel = idx, cnt
-        oracle.attention(case.dtype, case.q, case.k, case.v, case.idx, case.nsel, case.sinks, case.scale,
-                         False, threads=threads, lib=lib)
+        o = oracle.attention(case.dtype, case.q, case.k, case.v, case.idx, case.nsel, case.sinks, case.scale,
+                             False, threads=threads, lib=lib)
         t_total += time.perf_counter() - t0
+        g = out_host[r:r + 1].astype(np.float64)
+        fin = np.isfinite(o)
+        ok &= bool(np.array_equal(idx[0], idx_host[r]))
+        ok &= bool(np.array_equal(np.isnan(g), np.isnan(o)) and np.array_equal(np.isinf(g), np.isinf(o)))
+        err = np.abs(g[fin] - o[fin])
+        ok &= bool(np.all(err <= 2e-3 + 1e-2 * np.abs(o[fin])))
+        max_err = max(max_err, float(err.max()) if err.size else 0.0)
         rows_done += 1
-        r += 1
     value = rows_done * heads / t_total
-    return {"value": value, "unit": "query-rows*heads/s", "cores": threads, "kind": "oracle",
-            "sample": f"{rows_done} of the batch's rows (top-k over 4096 scores then 64-head attention "
-                      f"each), {t_total:.1f} s of float64 oracle work on {threads} OpenMP threads"}
+    base = {"value": value, "unit": "query-rows*heads/s", "cores": threads, "kind": "oracle",
+            "sample": f"the first {rows_done} of the batch's {max_rows} rows (top-k over the row's scores, "
+                      f"then {heads}-head attention), {t_total:.1f} s of float64 oracle work on "
+                      f"{threads} OpenMP threads"}
+    parity = {"rows": rows_done, "indices_bit_exact_and_attention_within_tol": ok, "max_abs_err": max_err}
+    return base, parity
 
 
 def main() -> int:
@@ -89,6 +102,9 @@ def main() -> int:
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--attn-only", action="store_true", help="time only the attention kernel (profiling)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB, --steps times "
+                         "(calibrates the HBM byte counters against a known size)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -101,9 +117,22 @@ def main() -> int:
     import sparse_attention_attn_amd as sa
     import workloads as w
 
-    sa.load()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) / args.steps
+        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "ms": dt * 1e3,
+                          "gbs_read_plus_write": 2 * n / dt / 1e9}), flush=True)
+        return 0
+    sa.load()
     B, H, N, K = args.batch, args.heads, args.n_ctx, args.k
 
     log(f"[bench] generating 2 input sets: {B} sequences x {N} positions x {w.D} bf16 K and V each")
@@ -153,8 +182,7 @@ def main() -> int:
         f"algorithmic ({achieved_gbs / HBM_PEAK_GBS:.1%} of 8 TB/s), "
         f"{flops / (attn_ms * 1e-3) / 1e12:.0f} TFLOP/s bf16 ({flops / (attn_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS:.1%} of MFMA peak)")
 
-    # Parity of this very launch configuration on two sampled rows (full checks live in tests/).
-    inp, scores, idx, cnt, out = sets[(args.steps - 1) % 2]
+    inp, scores, idx, cnt, out = sets[(args.steps - 1) % 2]  # the last timed step's set
     result = {
         "metric": "decode query-rows*heads/s (64 heads, d=512, k=640)",
         "value": B * H / (ms_per_step * 1e-3),
@@ -189,9 +217,10 @@ def main() -> int:
         },
         "cpu_baseline": None,
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not args.attn_only:
         log("[bench] timing the float64 oracle on the host")
-        result["cpu_baseline"] = cpu_baseline(inp, scores, H, K, args.cpu_budget, max_rows=B)
+        result["cpu_baseline"], result["parity_sampled"] = cpu_baseline(
+            inp, scores, out, inp["idx"] if args.attn_only else idx, H, K, args.cpu_budget, max_rows=B)
     print(json.dumps(result), flush=True)
     return 0
 

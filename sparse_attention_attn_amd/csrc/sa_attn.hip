@@ -17,19 +17,25 @@
 //     tile's K is in flight while the current tile's values are applied, and the
 //     next tile's V while the next scores are formed.
 //   * S^T = K Q^T and O^T = V^T P^T run on v_mfma_f32_32x32x16_bf16 with the heads
-//     on the N side, so every lane owns one head: the row maximum and the tile sum
-//     are an in-lane reduction over 16 scores plus one exchange with lane^32, and
-//     the two waves that split a tile's 64 keys combine their halves in LDS in a
-//     fixed order. V^T operands come from ds_read_b64_tr_b16 transposing reads.
+//     on the N side, so every lane owns one head. The two waves of a head block each
+//     hold the query for one half of the head width (64 VGPRs) and form partial
+//     scores for all 64 keys; each hands the other the partials of its key half
+//     through LDS, and both add (half 0 + half 1). The row maximum and the tile sum
+//     are then an in-lane reduction over 16 scores, one exchange with lane^32, and a
+//     fixed-order combine of the two key halves in LDS. V^T operands come from
+//     ds_read_b64_tr_b16 transposing reads.
 //   * Splitting work across workgroups only ever splits heads and output columns,
 //     never keys, so each (row, head, column) is produced by the same sequence of
 //     operations whatever the batch size or head count: results are bit-identical
 //     across launch shapes and repeats, and no workspace or combine pass exists.
 //
-// Numerics (the fixed order): per 64-key tile, m' = max(m, max_j s_j); the
-// reference r = m' unless m' = -inf, then 0; alpha = exp(m - r); p_j = exp(s_j - r)
-// rounded to bf16; l = alpha*l + sum_j p_j (the same rounded p); acc = alpha*acc +
-// P V; m = m'. Start: m = sink, l = exp(sink - r(sink)), acc = 0. End: acc / l.
+// Numerics (the fixed order), in log2 units (x2 = x * log2 e): per 64-key tile,
+// m' = max(m, max_j s_j); the exponent reference r moves to m' (0 if m' = -inf), with
+// alpha = 2^(r - r'), only when m' > r + 8 or r > m' > -inf for one of the wave's 32
+// heads, else alpha = 1; p_j = 2^(s_j - r) rounded to bf16; l = alpha*l + sum_j p_j
+// (the same rounded p); acc = alpha*acc + P V; m = m'. Start: m = sink, r = sink
+// (0 if -inf), l = 2^(sink - r), acc = 0. End: acc / l. The moves of r change only
+// rounding: every p stays below 2^8 and the ratio acc / l is what the definition gives.
 // Keys past a row's count score -inf by select and gather a zero row, so a tail
 // tile never multiplies a stale LDS value.
 #include <hip/hip_runtime.h>
@@ -51,6 +57,11 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kHeadDim = 512;   // sixteen 32-wide output column groups
 constexpr int kTile = 64;       // keys per online-softmax tile
 constexpr int kRowBytes = kHeadDim * 2;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLazy = 8.0f;  // log2 units: p <= 256 between reference moves
+
+// 2^x on the hardware exponential (v_exp_f32); exp2(-inf) = 0, exp2(+inf) = inf, NaN stays NaN.
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Source of the DMA for keys that are masked or invalid: 1 KiB of zeros.
 __device__ __attribute__((aligned(16))) const uint32_t g_zero_row[kRowBytes / 4] = {0};
@@ -120,8 +131,9 @@ __device__ __forceinline__ int64_t xcd_remap(int64_t i, int64_t G) {
 // Kernel template.
 //   HB: head blocks of 32 per workgroup (1 or 2); the workgroup has 2*HB waves.
 //   NT: 32-column output groups per wave; the workgroup covers 64*NT columns.
-// Wave w: head block hb = w/2; key half kb = w%2 of each tile for the scores; the
-// same kb picks which half of the workgroup's columns the wave accumulates.
+// Wave w: head block hb = w/2; kb = w%2 picks the half of the head width the wave
+// contracts for the scores, the 32-key block of each tile it finishes and
+// normalises, and the half of the workgroup's columns it accumulates.
 template <int HB, int NT>
 __global__ void __launch_bounds__(128 * HB) __attribute__((amdgpu_waves_per_eu(1, 1)))
 attn_bf16_kernel(AttnArgs a, int n_hg) {
@@ -138,7 +150,9 @@ attn_bf16_kernel(AttnArgs a, int n_hg) {
 
     __shared__ __attribute__((aligned(16))) char k_lds[kTile * kKStride];
     __shared__ __attribute__((aligned(16))) char v_lds[kTile * VSTRIDE];
-    __shared__ __attribute__((aligned(16))) bf16x8 p_lds[WAVES][2][64];
+    // Per-wave 4 KiB exchange slot: first the partial scores a wave hands its partner,
+    // later in the tile its P operand (the partner has read the partials by then).
+    __shared__ __attribute__((aligned(16))) float xch_lds[WAVES][16][64];
     __shared__ float max_lds[WAVES][32];
     __shared__ float sum_lds[WAVES][32];
     __shared__ int idx_lds[WAVES][2][64];   // each wave's own copy of a tile's index list
@@ -170,11 +184,12 @@ attn_bf16_kernel(AttnArgs a, int n_hg) {
     n = n < 0 ? 0 : (n > a.kmax ? a.kmax : n);
     const int ntiles = (n + kTile - 1) / kTile;
 
-    // Query operand of S^T = K Q^T: lane (head ln, half g) holds d = 256g + 8kk + 0..7.
-    bf16x8 qreg[32];
+    // Query operand of S^T = K Q^T over this wave's half kb of the head width: lane
+    // (head ln, half g) holds d = 256 kb + 128 g + 8 kk + 0..7, kk < 16.
+    bf16x8 qreg[16];
 #pragma unroll
-    for (int kk = 0; kk < 32; kk++) {
-        const bf16x8 v = *(const bf16x8 *)(qrow + 256 * g + 8 * kk);
+    for (int kk = 0; kk < 16; kk++) {
+        const bf16x8 v = *(const bf16x8 *)(qrow + 256 * kb + 128 * g + 8 * kk);
         qreg[kk] = head_ok ? v : qmask_zero;
     }
 
@@ -218,10 +233,14 @@ attn_bf16_kernel(AttnArgs a, int n_hg) {
         }
     };
 
-    const float sink = head_ok ? a.sinks[head] : 0.0f;
-    float m_run = sink;
-    const float r0 = (sink == -INFINITY) ? 0.0f : sink;
-    float l_run = expf(sink - r0);
+    // Softmax state in log2 units: scores and the sink are multiplied by log2(e) so that
+    // exp(x - y) = exp2(x2 - y2) runs on v_exp_f32. m_run is the running maximum, ref the
+    // exponent reference that l_run and acc are relative to (see the tile update).
+    const float scale2 = a.scale * kLog2e;
+    const float sink2 = (head_ok ? a.sinks[head] : 0.0f) * kLog2e;
+    float m_run = sink2;
+    float ref = (sink2 == -INFINITY) ? 0.0f : sink2;
+    float l_run = exp2_hw(sink2 - ref);
     f32x16 acc[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; nt++) acc[nt] = (f32x16){};
@@ -247,29 +266,36 @@ attn_bf16_kernel(AttnArgs a, int n_hg) {
             wait_vmcnt<NV + 1>();
             lds_barrier();
 
-            // ---- scores S^T (32 keys of half kb) x (32 heads), K from LDS, Q in registers.
-            f32x16 sacc = (f32x16){};
+            // ---- partial scores over this wave's half kb of the head width, for both
+            // 32-key blocks of the tile: S^T (keys) x (32 heads); K from LDS, Q in registers.
+            f32x16 sacc0 = (f32x16){}, sacc1 = (f32x16){};
             {
-                const SA_LDS char *krow = (const SA_LDS char *)k_lds + (kb * 32 + ln) * kKStride + 512 * g;
+                // Software-pipelined: the operands of step kk+1 are read before the two
+                // MFMAs of step kk issue, so LDS latency hides behind the matrix pipe.
+                const SA_LDS char *krow = (const SA_LDS char *)k_lds + ln * kKStride + 512 * kb + 256 * g;
+                bf16x8 k0 = *(const SA_LDS bf16x8 *)(krow);
+                bf16x8 k1 = *(const SA_LDS bf16x8 *)(krow + 32 * kKStride);
 #pragma unroll
-                for (int kk = 0; kk < 32; kk++) {
-                    const bf16x8 kop = *(const SA_LDS bf16x8 *)(krow + 16 * kk);
-                    sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qreg[kk], sacc, 0, 0, 0);
-                    if ((kk & 7) == 7) __builtin_amdgcn_sched_barrier(0);
+                for (int kk = 0; kk < 16; kk++) {
+                    bf16x8 n0 = k0, n1 = k1;
+                    if (kk + 1 < 16) {
+                        n0 = *(const SA_LDS bf16x8 *)(krow + 16 * (kk + 1));
+                        n1 = *(const SA_LDS bf16x8 *)(krow + 32 * kKStride + 16 * (kk + 1));
+                    }
+                    sacc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qreg[kk], sacc0, 0, 0, 0);
+                    sacc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qreg[kk], sacc1, 0, 0, 0);
+                    __builtin_amdgcn_sched_barrier(0);
+                    k0 = n0;
+                    k1 = n1;
                 }
             }
-            // Element e of this lane is key kb*32 + 16*(e/8) + 8g + e%8 of the tile.
-            float s[16];
-            float mloc = -INFINITY;
+            // Hand the partner (the other half of the head width) its key block's partials.
+            {
+                const f32x16 give = kb ? sacc0 : sacc1;
 #pragma unroll
-            for (int e = 0; e < 16; e++) {
-                const int p = t * kTile + kb * 32 + 16 * (e >> 3) + 8 * g + (e & 7);
-                s[e] = p < n ? sacc[e] * a.scale : -INFINITY;
-                mloc = fmaxf(mloc, s[e]);
+                for (int e = 0; e < 16; e++) xch_lds[w][e][lane] = give[e];
             }
-            mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-            if (g == 0) max_lds[w][ln] = mloc;
-            lds_barrier();  // every wave is also done reading k_lds
+            lds_barrier();  // partials exchanged; every wave is also done reading k_lds
 
             // Indices of tile t+1 have landed; start gathering its K.
             wait_vmcnt<NV>();
@@ -279,22 +305,51 @@ attn_bf16_kernel(AttnArgs a, int n_hg) {
                 dma_k(iv_n);
             }
 
-            // ---- online softmax with the sink, fixed order.
+            // Full scores of key block kb: (half 0 + half 1) of the head width, the same
+            // sum in both waves of the pair. Element e of this lane is key
+            // kb*32 + 16*(e/8) + 8g + e%8 of the tile.
+            const f32x16 own = kb ? sacc1 : sacc0;
+            float s[16];
+            float mloc = -INFINITY;
+#pragma unroll
+            for (int e = 0; e < 16; e++) {
+                const float full = own[e] + xch_lds[w ^ 1][e][lane];
+                const int p = t * kTile + kb * 32 + 16 * (e >> 3) + 8 * g + (e & 7);
+                s[e] = p < n ? full * scale2 : -INFINITY;
+                mloc = fmaxf(mloc, s[e]);
+            }
+            mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+            if (g == 0) max_lds[w][ln] = mloc;
+            lds_barrier();  // maxima exchanged; every wave is done reading the partials
+
+            // ---- online softmax with the sink, fixed order. The reference follows the
+            // running maximum lazily: it moves (and l_run, acc are rescaled by alpha) only
+            // when the maximum has risen more than kLazy above it, or when it sits above a
+            // finite maximum (only possible from the start value 0 of a -inf sink); the
+            // decision is taken for the wave's 32 heads together. Otherwise alpha = 1 and
+            // the accumulators are left alone; every p stays <= 2^kLazy.
             const float mt = fmaxf(max_lds[2 * hb][ln], max_lds[2 * hb + 1][ln]);
             const float m_new = fmaxf(m_run, mt);
-            const float ref = (m_new == -INFINITY) ? 0.0f : m_new;
-            const float alpha = expf(m_run - ref);
+            const bool move = m_new > ref + kLazy || (m_new < ref && m_new != -INFINITY);
+            const bool rescale = __builtin_amdgcn_ballot_w64(move) != 0;
+            float alpha = 1.0f;
+            if (rescale) {
+                const float ref_new = (m_new == -INFINITY) ? 0.0f : m_new;
+                alpha = exp2_hw(ref - ref_new);
+                ref = ref_new;
+            }
             bf16x8 pk0, pk1;
             float psum = 0.0f;
 #pragma unroll
             for (int e = 0; e < 16; e++) {
-                const __bf16 pb = (__bf16)expf(s[e] - ref);
+                const __bf16 pb = (__bf16)exp2_hw(s[e] - ref);
                 psum += (float)pb;
                 if (e < 8) pk0[e] = pb; else pk1[e - 8] = pb;
             }
             psum += __shfl_xor(psum, 32);
-            p_lds[w][0][lane] = pk0;
-            p_lds[w][1][lane] = pk1;
+            bf16x8 *p_out = (bf16x8 *)&xch_lds[w][0][0];
+            p_out[lane] = pk0;
+            p_out[64 + lane] = pk1;
             if (g == 0) sum_lds[w][ln] = psum;
 
             // V(t) has landed (K(t+1) may be in flight).
@@ -304,10 +359,18 @@ attn_bf16_kernel(AttnArgs a, int n_hg) {
             l_run = alpha * l_run + (sum_lds[2 * hb][ln] + sum_lds[2 * hb + 1][ln]);
             m_run = m_new;
 
+            if (rescale) [[unlikely]] {
+#pragma unroll
+                for (int nt = 0; nt < NT; nt++) {
+                    acc[nt] *= alpha;
+                    __builtin_amdgcn_sched_barrier(0);  // one 16-register group at a time
+                }
+            }
+
             // ---- values O^T += V^T P^T over the tile's four 16-key steps.
             bf16x8 pop[4];
 #pragma unroll
-            for (int ks = 0; ks < 4; ks++) pop[ks] = p_lds[2 * hb + (ks >> 1)][ks & 1][lane];
+            for (int ks = 0; ks < 4; ks++) pop[ks] = ((const bf16x8 *)&xch_lds[2 * hb + (ks >> 1)][0][0])[64 * (ks & 1) + lane];
             // Lane (g, ch, l16) addresses row 16ks + 8g + 4t2 + l16/4 and columns
             // 32nt + 16ch + 4(l16%4) .. +3 of the wave's half of the slice; the
             // transposing read returns column 32nt + 16ch + l16 of rows +0..3.
@@ -315,26 +378,35 @@ attn_bf16_kernel(AttnArgs a, int n_hg) {
             const int ch = (lane >> 4) & 1;
             const SA_LDS char *vrow = (const SA_LDS char *)v_lds + (8 * g + (l16 >> 2)) * VSTRIDE +
                                       2 * (kb * NT * 32 + 16 * ch + 4 * (l16 & 3));
-#pragma unroll
-            for (int nt = 0; nt < NT; nt++) {
-                acc[nt] *= alpha;
+            // Software-pipelined over the column groups: the four V^T operands of group
+            // nt+1 (eight transposing reads) are issued before the four MFMAs of group nt.
+            auto read_v = [&](int nt, bf16x8 (&vop)[4]) {
 #pragma unroll
                 for (int ks = 0; ks < 4; ks++) {
-                    bf16x8 vop;
 #pragma unroll
                     for (int t2 = 0; t2 < 2; t2++) {
                         const bf16x4 part = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
                             (SA_LDS bf16x4 *)(vrow + (16 * ks + 4 * t2) * VSTRIDE + 64 * nt));
-                        vop[4 * t2 + 0] = part[0];
-                        vop[4 * t2 + 1] = part[1];
-                        vop[4 * t2 + 2] = part[2];
-                        vop[4 * t2 + 3] = part[3];
+                        vop[ks][4 * t2 + 0] = part[0];
+                        vop[ks][4 * t2 + 1] = part[1];
+                        vop[ks][4 * t2 + 2] = part[2];
+                        vop[ks][4 * t2 + 3] = part[3];
                     }
-                    acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pop[ks], acc[nt], 0, 0, 0);
                 }
+            };
+            bf16x8 vcur[4], vnxt[4];
+            read_v(0, vcur);
+#pragma unroll
+            for (int nt = 0; nt < NT; nt++) {
+                if (nt + 1 < NT) read_v(nt + 1, vnxt);
+#pragma unroll
+                for (int ks = 0; ks < 4; ks++)
+                    acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vcur[ks], pop[ks], acc[nt], 0, 0, 0);
                 __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int ks = 0; ks < 4; ks++) vcur[ks] = vnxt[ks];
             }
-            lds_barrier();  // every wave is done with v_lds and p_lds
+            lds_barrier();  // every wave is done with v_lds and the P operands
 
             dma_idx(t + 2, t & 1);  // slot t&1 held tile t's list, consumed above
             if (more) dma_v(iv_n);
@@ -367,7 +439,7 @@ hipError_t launch_variant(const AttnArgs &a, int64_t grid, hipStream_t s) {
 }
 
 constexpr int lds_bytes_of(int HB, int NT) {
-    return kTile * kKStride + kTile * (128 * NT + 64) + 2 * HB * 2 * 64 * 16 + 2 * 2 * HB * 32 * 4;
+    return kTile * kKStride + kTile * (128 * NT + 64) + 2 * HB * 4096 + 2 * 2 * HB * 32 * 4 + 2 * HB * 512;
 }
 
 }  // namespace

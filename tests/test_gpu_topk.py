@@ -86,3 +86,12 @@ def test_empty():
     idx, cnt = sa.topk(s, 10)
     torch.cuda.synchronize()
     assert idx.shape == (0, 10)
+
+
+def test_mid_rows_four_waves():
+    """Rows of 4,097..16,384 scores (four waves per row) with ragged valid lengths."""
+    rng = np.random.default_rng(74)
+    s = rng.standard_normal((5, 10000)).astype(np.float32)
+    s[2, 5000:7000] = 0.25
+    check(s, 640, np.array([10000, 4097, 6500, 700, 9999], np.int32), label="n=10000")
+    check(np.round(s * 8) / 8, 1000, label="n=10000 ties")
