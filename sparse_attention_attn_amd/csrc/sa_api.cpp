@@ -58,7 +58,7 @@ int check_attn(int dtype, const void *q, const void *k, const void *v, int64_t n
         return fail(SA_ERR_UNSUPPORTED, "idx, nsel and sinks must be 4-byte aligned");
     if (dtype == SA_BF16) {
         const sa::AttnPlan p = sa::plan_attn_bf16(rows, H);
-        if (p.grid > kMaxGrid) return fail(SA_ERR_SHAPE, "too many rows for one launch");
+        if (p.units > kMaxGrid) return fail(SA_ERR_SHAPE, "too many rows for one launch");
     } else if ((int64_t)rows * H > kMaxGrid) {
         return fail(SA_ERR_SHAPE, "too many rows for one launch");
     }

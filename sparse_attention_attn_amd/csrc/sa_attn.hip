@@ -42,6 +42,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "sa_internal.h"
 
 namespace sa {
@@ -136,7 +138,7 @@ __device__ __forceinline__ int64_t xcd_remap(int64_t i, int64_t G) {
 // normalises, and the half of the workgroup's columns it accumulates.
 template <int HB, int NT>
 __global__ void __launch_bounds__(128 * HB) __attribute__((amdgpu_waves_per_eu(1, 1)))
-attn_bf16_kernel(AttnArgs a, int n_hg) {
+attn_bf16_kernel(AttnArgs a, int n_hg, int64_t units) {
     constexpr int WAVES = 2 * HB;
     constexpr int COLS = 64 * NT;              // output columns per workgroup
     constexpr int VROW = COLS * 2;             // bytes of one V row slice
@@ -164,56 +166,66 @@ attn_bf16_kernel(AttnArgs a, int n_hg) {
     const int hb = w >> 1;
     const int kb = w & 1;
 
+    // A unit is one (query row, head group, column slice). This workgroup serves units
+    // base, base + G, base + 2G, ... as one stream of 64-key tiles, so the next unit's
+    // first gathers overlap the current unit's last tile. Every unit has at least one
+    // tile (a row with no selected key runs one all-masked tile, which changes nothing).
     const int64_t G = (int64_t)gridDim.x;
-    const int64_t lid = xcd_remap(blockIdx.x, G);
-    const int cs = (int)(lid % N_CS);
-    const int hg = (int)((lid / N_CS) % n_hg);
-    const int64_t row = lid / ((int64_t)N_CS * n_hg);
+    const int64_t base = xcd_remap(blockIdx.x, G);
 
-    const int head = (hg * HB + hb) * 32 + ln;
-    const bool head_ok = head < a.H;
-    const int col0 = cs * COLS + kb * NT * 32;        // first output column of this wave
-
-    // Heads past H (internal padding to the 32-head block) read head 0 and are zeroed.
-    const uint16_t *qrow = (const uint16_t *)a.q + ((int64_t)row * a.H + (head_ok ? head : 0)) * kHeadDim;
-    const bf16x8 qmask_zero = (bf16x8){};
-    const char *kbase = (const char *)a.k + (int64_t)row * a.cache_stride * 2;
-    const char *vbase = (const char *)a.v + (int64_t)row * a.cache_stride * 2 + (int64_t)cs * VROW;
-    const int32_t *irow = a.idx + (int64_t)row * a.kmax;
-    int n = a.nsel ? a.nsel[row] : a.kmax;
-    n = n < 0 ? 0 : (n > a.kmax ? a.kmax : n);
-    const int ntiles = (n + kTile - 1) / kTile;
-
-    // Query operand of S^T = K Q^T over this wave's half kb of the head width: lane
-    // (head ln, half g) holds d = 256 kb + 128 g + 8 kk + 0..7, kk < 16.
-    bf16x8 qreg[16];
-#pragma unroll
-    for (int kk = 0; kk < 16; kk++) {
-        const bf16x8 v = *(const bf16x8 *)(qrow + 256 * kb + 128 * g + 8 * kk);
-        qreg[kk] = head_ok ? v : qmask_zero;
-    }
-
-    // Index list of tile t into this wave's slot buf: lane l fetches entry t*64 + l
-    // (address clamped to the row, so the fetch is always issued: every wave then
-    // issues the same number of vector-memory operations per tile).
-    auto dma_idx = [&](int t, int buf) {
-        const int p = t * kTile + lane;
-        const int pc = p < a.kmax ? p : a.kmax - 1;
-        dma4(irow, (uint32_t)pc * 4u, lds_addr(&idx_lds[w][buf][0]));
+    struct Item {          // one tile of one unit (all fields wave-uniform)
+        int64_t unit;      // < 0: none
+        int64_t row;
+        int tile, ntiles, n, hg, cs;
     };
-    // Row to gather for entry t*64 + l, or -1 (masked or out of range: gather zeros).
-    auto resolve = [&](int t, int buf, bool &bad) -> int {
+    auto make_item = [&](int64_t u) -> Item {
+        Item it{};
+        it.unit = u;
+        if (u < 0 || u >= units) { it.unit = -1; return it; }
+        it.cs = (int)(u % N_CS);
+        it.hg = (int)((u / N_CS) % n_hg);
+        it.row = u / ((int64_t)N_CS * n_hg);
+        int n = a.nsel ? a.nsel[it.row] : a.kmax;
+        n = n < 0 ? 0 : (n > a.kmax ? a.kmax : n);
+        it.n = n;
+        it.tile = 0;
+        it.ntiles = n > 0 ? (n + kTile - 1) / kTile : 1;
+        return it;
+    };
+    auto next_item = [&](const Item &it) -> Item {
+        if (it.unit < 0) return it;
+        if (it.tile + 1 < it.ntiles) { Item nx = it; nx.tile++; return nx; }
+        return make_item(it.unit + G);
+    };
+    auto idx_row = [&](const Item &it) { return a.idx + it.row * a.kmax; };
+    auto kbase_of = [&](const Item &it) { return (const char *)a.k + it.row * a.cache_stride * 2; };
+    auto vbase_of = [&](const Item &it) {
+        return (const char *)a.v + it.row * a.cache_stride * 2 + (int64_t)it.cs * VROW;
+    };
+
+    // Index list of an item's tile into this wave's slot buf: lane l fetches entry
+    // tile*64 + l (address clamped to the row). Always issued, also when there is no
+    // item (then the current row's list is re-read), so that every wave issues the same
+    // number of vector-memory operations per tile.
+    auto dma_idx = [&](const Item &it, const Item &fallback, int buf) {
+        const Item &src = it.unit >= 0 ? it : fallback;
+        const int p = (it.unit >= 0 ? it.tile : 0) * kTile + lane;
+        const int pc = p < a.kmax ? p : a.kmax - 1;
+        dma4(idx_row(src), (uint32_t)pc * 4u, lds_addr(&idx_lds[w][buf][0]));
+    };
+    // Row to gather for entry tile*64 + l, or -1 (masked or out of range: gather zeros).
+    auto resolve = [&](const Item &it, int buf, bool &bad) -> int {
         const int iv = idx_lds[w][buf][lane];
-        const int p = t * kTile + lane;
-        const bool live = p < n;
+        const int p = it.tile * kTile + lane;
+        const bool live = p < it.n;
         const bool inr = iv >= 0 && (int64_t)iv < a.n_ctx;
         if (__builtin_amdgcn_ballot_w64(live && !inr)) bad = true;
         return (live && inr) ? iv : -1;
     };
-
     // One DMA instruction gathers one cache row (64 lanes x 16 bytes = 1 KiB) into
     // an LDS slot; lane i moves bytes [16i, 16i + 16) of the row.
-    auto dma_k = [&](int iv) {
+    auto dma_k = [&](const Item &it, int iv) {
+        const char *kbase = kbase_of(it);
 #pragma unroll
         for (int i = 0; i < NK; i++) {
             const int slot = w * NK + i;
@@ -222,8 +234,9 @@ attn_bf16_kernel(AttnArgs a, int n_hg) {
             dma16(rbase, (uint32_t)lane << 4, lds_addr(k_lds + slot * kKStride));
         }
     };
-    // V rows keep the tile's key order; only this workgroup's column slice is moved.
-    auto dma_v = [&](int iv) {
+    // V rows keep the tile's key order; only the unit's column slice is moved.
+    auto dma_v = [&](const Item &it, int iv) {
+        const char *vbase = vbase_of(it);
 #pragma unroll
         for (int i = 0; i < NV; i++) {
             const int j = w * NV + i;
@@ -233,208 +246,242 @@ attn_bf16_kernel(AttnArgs a, int n_hg) {
         }
     };
 
+    // Per-unit state. Query operand of S^T = K Q^T over this wave's half kb of the head
+    // width: lane (head ln, half g) holds d = 256 kb + 128 g + 8 kk + 0..7, kk < 16.
+    // Heads past H (internal padding to the 32-head block) read head 0 and are zeroed.
     // Softmax state in log2 units: scores and the sink are multiplied by log2(e) so that
     // exp(x - y) = exp2(x2 - y2) runs on v_exp_f32. m_run is the running maximum, ref the
     // exponent reference that l_run and acc are relative to (see the tile update).
     const float scale2 = a.scale * kLog2e;
-    const float sink2 = (head_ok ? a.sinks[head] : 0.0f) * kLog2e;
-    float m_run = sink2;
-    float ref = (sink2 == -INFINITY) ? 0.0f : sink2;
-    float l_run = exp2_hw(sink2 - ref);
+    bf16x8 qreg[16];
     f32x16 acc[NT];
+    float m_run, ref, l_run;
+    int head;
+    bool head_ok;
+    // Issues the unit's query and sink loads (the compiler's own); the caller drains them.
+    auto enter_unit = [&](const Item &it) {
+        head = (it.hg * HB + hb) * 32 + ln;
+        head_ok = head < a.H;
+        const uint16_t *qrow = (const uint16_t *)a.q + (it.row * a.H + (head_ok ? head : 0)) * kHeadDim;
 #pragma unroll
-    for (int nt = 0; nt < NT; nt++) acc[nt] = (f32x16){};
-    bool bad = false;
-
-    // The query and sink loads above are the compiler's own; let them complete here
-    // so that nothing the compiler tracks is pending inside the loop.
-    __builtin_amdgcn_s_waitcnt(0);
-
-    if (ntiles > 0) {
-        // Issue order per wave: K(0), I(1), V(0); then in iteration t: K(t+1) after the
-        // scores, I(t+2) and V(t+1) after the values.
-        dma_idx(0, 0);
-        wait_vmcnt<0>();
-        const int iv0 = resolve(0, 0, bad);
-        dma_k(iv0);
-        dma_idx(1, 1);
-        dma_v(iv0);
-
-        for (int t = 0; t < ntiles; t++) {
-            const bool more = t + 1 < ntiles;
-            // K(t) has landed for this wave (I(t+1) and V(t) may be in flight).
-            wait_vmcnt<NV + 1>();
-            lds_barrier();
-
-            // ---- partial scores over this wave's half kb of the head width, for both
-            // 32-key blocks of the tile: S^T (keys) x (32 heads); K from LDS, Q in registers.
-            f32x16 sacc0 = (f32x16){}, sacc1 = (f32x16){};
-            {
-                // Software-pipelined: the operands of step kk+1 are read before the two
-                // MFMAs of step kk issue, so LDS latency hides behind the matrix pipe.
-                const SA_LDS char *krow = (const SA_LDS char *)k_lds + ln * kKStride + 512 * kb + 256 * g;
-                bf16x8 k0 = *(const SA_LDS bf16x8 *)(krow);
-                bf16x8 k1 = *(const SA_LDS bf16x8 *)(krow + 32 * kKStride);
+        for (int kk = 0; kk < 16; kk++) {
+            const bf16x8 v = *(const bf16x8 *)(qrow + 256 * kb + 128 * g + 8 * kk);
+            qreg[kk] = head_ok ? v : (bf16x8){};
+        }
+        const float sink2 = (head_ok ? a.sinks[head] : 0.0f) * kLog2e;
+        m_run = sink2;
+        ref = (sink2 == -INFINITY) ? 0.0f : sink2;
+        l_run = exp2_hw(sink2 - ref);
 #pragma unroll
-                for (int kk = 0; kk < 16; kk++) {
-                    bf16x8 n0 = k0, n1 = k1;
-                    if (kk + 1 < 16) {
-                        n0 = *(const SA_LDS bf16x8 *)(krow + 16 * (kk + 1));
-                        n1 = *(const SA_LDS bf16x8 *)(krow + 32 * kKStride + 16 * (kk + 1));
-                    }
-                    sacc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qreg[kk], sacc0, 0, 0, 0);
-                    sacc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qreg[kk], sacc1, 0, 0, 0);
-                    __builtin_amdgcn_sched_barrier(0);
-                    k0 = n0;
-                    k1 = n1;
-                }
-            }
-            // Hand the partner (the other half of the head width) its key block's partials.
-            {
-                const f32x16 give = kb ? sacc0 : sacc1;
-#pragma unroll
-                for (int e = 0; e < 16; e++) xch_lds[w][e][lane] = give[e];
-            }
-            lds_barrier();  // partials exchanged; every wave is also done reading k_lds
-
-            // Indices of tile t+1 have landed; start gathering its K.
-            wait_vmcnt<NV>();
-            int iv_n = 0;
-            if (more) {
-                iv_n = resolve(t + 1, (t + 1) & 1, bad);
-                dma_k(iv_n);
-            }
-
-            // Full scores of key block kb: (half 0 + half 1) of the head width, the same
-            // sum in both waves of the pair. Element e of this lane is key
-            // kb*32 + 16*(e/8) + 8g + e%8 of the tile.
-            const f32x16 own = kb ? sacc1 : sacc0;
-            float s[16];
-            float mloc = -INFINITY;
-#pragma unroll
-            for (int e = 0; e < 16; e++) {
-                const float full = own[e] + xch_lds[w ^ 1][e][lane];
-                const int p = t * kTile + kb * 32 + 16 * (e >> 3) + 8 * g + (e & 7);
-                s[e] = p < n ? full * scale2 : -INFINITY;
-                mloc = fmaxf(mloc, s[e]);
-            }
-            mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-            if (g == 0) max_lds[w][ln] = mloc;
-            lds_barrier();  // maxima exchanged; every wave is done reading the partials
-
-            // ---- online softmax with the sink, fixed order. The reference follows the
-            // running maximum lazily: it moves (and l_run, acc are rescaled by alpha) only
-            // when the maximum has risen more than kLazy above it, or when it sits above a
-            // finite maximum (only possible from the start value 0 of a -inf sink); the
-            // decision is taken for the wave's 32 heads together. Otherwise alpha = 1 and
-            // the accumulators are left alone; every p stays <= 2^kLazy.
-            const float mt = fmaxf(max_lds[2 * hb][ln], max_lds[2 * hb + 1][ln]);
-            const float m_new = fmaxf(m_run, mt);
-            const bool move = m_new > ref + kLazy || (m_new < ref && m_new != -INFINITY);
-            const bool rescale = __builtin_amdgcn_ballot_w64(move) != 0;
-            float alpha = 1.0f;
-            if (rescale) {
-                const float ref_new = (m_new == -INFINITY) ? 0.0f : m_new;
-                alpha = exp2_hw(ref - ref_new);
-                ref = ref_new;
-            }
-            bf16x8 pk0, pk1;
-            float psum = 0.0f;
-#pragma unroll
-            for (int e = 0; e < 16; e++) {
-                const __bf16 pb = (__bf16)exp2_hw(s[e] - ref);
-                psum += (float)pb;
-                if (e < 8) pk0[e] = pb; else pk1[e - 8] = pb;
-            }
-            psum += __shfl_xor(psum, 32);
-            bf16x8 *p_out = (bf16x8 *)&xch_lds[w][0][0];
-            p_out[lane] = pk0;
-            p_out[64 + lane] = pk1;
-            if (g == 0) sum_lds[w][ln] = psum;
-
-            // V(t) has landed (K(t+1) may be in flight).
-            if (more) wait_vmcnt<NK>(); else wait_vmcnt<0>();
-            lds_barrier();
-
-            l_run = alpha * l_run + (sum_lds[2 * hb][ln] + sum_lds[2 * hb + 1][ln]);
-            m_run = m_new;
-
-            if (rescale) [[unlikely]] {
-#pragma unroll
-                for (int nt = 0; nt < NT; nt++) {
-                    acc[nt] *= alpha;
-                    __builtin_amdgcn_sched_barrier(0);  // one 16-register group at a time
-                }
-            }
-
-            // ---- values O^T += V^T P^T over the tile's four 16-key steps.
-            bf16x8 pop[4];
-#pragma unroll
-            for (int ks = 0; ks < 4; ks++) pop[ks] = ((const bf16x8 *)&xch_lds[2 * hb + (ks >> 1)][0][0])[64 * (ks & 1) + lane];
-            // Lane (g, ch, l16) addresses row 16ks + 8g + 4t2 + l16/4 and columns
-            // 32nt + 16ch + 4(l16%4) .. +3 of the wave's half of the slice; the
-            // transposing read returns column 32nt + 16ch + l16 of rows +0..3.
-            const int l16 = lane & 15;
-            const int ch = (lane >> 4) & 1;
-            const SA_LDS char *vrow = (const SA_LDS char *)v_lds + (8 * g + (l16 >> 2)) * VSTRIDE +
-                                      2 * (kb * NT * 32 + 16 * ch + 4 * (l16 & 3));
-            // Software-pipelined over the column groups: the four V^T operands of group
-            // nt+1 (eight transposing reads) are issued before the four MFMAs of group nt.
-            auto read_v = [&](int nt, bf16x8 (&vop)[4]) {
-#pragma unroll
-                for (int ks = 0; ks < 4; ks++) {
-#pragma unroll
-                    for (int t2 = 0; t2 < 2; t2++) {
-                        const bf16x4 part = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                            (SA_LDS bf16x4 *)(vrow + (16 * ks + 4 * t2) * VSTRIDE + 64 * nt));
-                        vop[ks][4 * t2 + 0] = part[0];
-                        vop[ks][4 * t2 + 1] = part[1];
-                        vop[ks][4 * t2 + 2] = part[2];
-                        vop[ks][4 * t2 + 3] = part[3];
-                    }
-                }
-            };
-            bf16x8 vcur[4], vnxt[4];
-            read_v(0, vcur);
+        for (int nt = 0; nt < NT; nt++) acc[nt] = (f32x16){};
+    };
+    // Normalise and store: lane holds head ln, columns col0 + 32nt + 8(e/4) + 4g + e%4.
+    auto leave_unit = [&](const Item &it, bool bad) {
+        if (head_ok) {
+            const int col0 = it.cs * COLS + kb * NT * 32;
+            float *orow = a.out + (it.row * a.H + head) * kHeadDim;
 #pragma unroll
             for (int nt = 0; nt < NT; nt++) {
-                if (nt + 1 < NT) read_v(nt + 1, vnxt);
 #pragma unroll
-                for (int ks = 0; ks < 4; ks++)
-                    acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vcur[ks], pop[ks], acc[nt], 0, 0, 0);
-                __builtin_amdgcn_sched_barrier(0);
+                for (int eq = 0; eq < 4; eq++) {
+                    f32x4 o;
 #pragma unroll
-                for (int ks = 0; ks < 4; ks++) vcur[ks] = vnxt[ks];
+                    for (int i = 0; i < 4; i++) o[i] = bad ? NAN : acc[nt][4 * eq + i] / l_run;
+                    *(f32x4 *)(orow + col0 + 32 * nt + 8 * eq + 4 * g) = o;
+                }
             }
-            lds_barrier();  // every wave is done with v_lds and the P operands
-
-            dma_idx(t + 2, t & 1);  // slot t&1 held tile t's list, consumed above
-            if (more) dma_v(iv_n);
         }
-        wait_vmcnt<0>();
+    };
+
+    // Issue order per wave: K(j), I(j+1), V(j) for the first item j = 0; then in
+    // iteration j: K(j+1) after the scores; I(j+2) and V(j+1) after the values. At the
+    // end of a unit: its outputs, the next unit's query and sink, and one full drain.
+    Item cur = make_item(base);
+    Item nx = next_item(cur);
+    Item nx2 = next_item(nx);
+    bool bad = false, bad_next = false;
+    enter_unit(cur);
+    dma_idx(cur, cur, 0);
+    __builtin_amdgcn_s_waitcnt(0);  // nothing the compiler tracks is pending in the loop
+    {
+        const int iv0 = resolve(cur, 0, bad);
+        dma_k(cur, iv0);
+        dma_idx(nx, cur, 1);
+        dma_v(cur, iv0);
     }
 
-    // ---- normalise and store: lane holds head ln, columns col0 + 32nt + 8(e/4) + 4g + e%4.
-    if (head_ok) {
-        float *orow = a.out + ((int64_t)row * a.H + head) * kHeadDim;
-        const float inv_nan = bad ? NAN : 0.0f;
+    for (int j = 0; cur.unit >= 0; j++) {
+        const bool more = nx.unit >= 0;
+        const bool last_of_unit = !more || nx.unit != cur.unit;
+        // K(j) has landed for this wave (I(j+1) and V(j) may be in flight).
+        wait_vmcnt<NV + 1>();
+        lds_barrier();
+
+        // ---- partial scores over this wave's half kb of the head width, for both
+        // 32-key blocks of the tile: S^T (keys) x (32 heads); K from LDS, Q in registers.
+        f32x16 sacc0 = (f32x16){}, sacc1 = (f32x16){};
+        {
+            // Software-pipelined: the operands of step kk+1 are read before the two
+            // MFMAs of step kk issue, so LDS latency hides behind the matrix pipe.
+            const SA_LDS char *krow = (const SA_LDS char *)k_lds + ln * kKStride + 512 * kb + 256 * g;
+            bf16x8 k0 = *(const SA_LDS bf16x8 *)(krow);
+            bf16x8 k1 = *(const SA_LDS bf16x8 *)(krow + 32 * kKStride);
+#pragma unroll
+            for (int kk = 0; kk < 16; kk++) {
+                bf16x8 n0 = k0, n1 = k1;
+                if (kk + 1 < 16) {
+                    n0 = *(const SA_LDS bf16x8 *)(krow + 16 * (kk + 1));
+                    n1 = *(const SA_LDS bf16x8 *)(krow + 32 * kKStride + 16 * (kk + 1));
+                }
+                sacc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qreg[kk], sacc0, 0, 0, 0);
+                sacc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qreg[kk], sacc1, 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+                k0 = n0;
+                k1 = n1;
+            }
+        }
+        // Hand the partner (the other half of the head width) its key block's partials.
+        {
+            const f32x16 give = kb ? sacc0 : sacc1;
+#pragma unroll
+            for (int e = 0; e < 16; e++) xch_lds[w][e][lane] = give[e];
+        }
+        lds_barrier();  // partials exchanged; every wave is also done reading k_lds
+
+        // Indices of item j+1 have landed; start gathering its K.
+        wait_vmcnt<NV>();
+        int iv_n = 0;
+        if (more) {
+            iv_n = resolve(nx, (j + 1) & 1, nx.unit == cur.unit ? bad : bad_next);
+            dma_k(nx, iv_n);
+        }
+
+        // Full scores of key block kb: (half 0 + half 1) of the head width, the same
+        // sum in both waves of the pair. Element e of this lane is key
+        // kb*32 + 16*(e/8) + 8g + e%8 of the tile.
+        const f32x16 own = kb ? sacc1 : sacc0;
+        float s[16];
+        float mloc = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < 16; e++) {
+            const float full = own[e] + xch_lds[w ^ 1][e][lane];
+            const int p = cur.tile * kTile + kb * 32 + 16 * (e >> 3) + 8 * g + (e & 7);
+            s[e] = p < cur.n ? full * scale2 : -INFINITY;
+            mloc = fmaxf(mloc, s[e]);
+        }
+        mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+        if (g == 0) max_lds[w][ln] = mloc;
+        lds_barrier();  // maxima exchanged; every wave is done reading the partials
+
+        // ---- online softmax with the sink, fixed order. The reference follows the
+        // running maximum lazily: it moves (and l_run, acc are rescaled by alpha) only
+        // when the maximum has risen more than kLazy above it, or when it sits above a
+        // finite maximum (only possible from the start value 0 of a -inf sink); the
+        // decision is taken for the wave's 32 heads together. Otherwise alpha = 1 and
+        // the accumulators are left alone; every p stays <= 2^kLazy.
+        const float mt = fmaxf(max_lds[2 * hb][ln], max_lds[2 * hb + 1][ln]);
+        const float m_new = fmaxf(m_run, mt);
+        const bool move = m_new > ref + kLazy || (m_new < ref && m_new != -INFINITY);
+        const bool rescale = __builtin_amdgcn_ballot_w64(move) != 0;
+        float alpha = 1.0f;
+        if (rescale) {
+            const float ref_new = (m_new == -INFINITY) ? 0.0f : m_new;
+            alpha = exp2_hw(ref - ref_new);
+            ref = ref_new;
+        }
+        bf16x8 pk0, pk1;
+        float psum = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 16; e++) {
+            const __bf16 pb = (__bf16)exp2_hw(s[e] - ref);
+            psum += (float)pb;
+            if (e < 8) pk0[e] = pb; else pk1[e - 8] = pb;
+        }
+        psum += __shfl_xor(psum, 32);
+        bf16x8 *p_out = (bf16x8 *)&xch_lds[w][0][0];
+        p_out[lane] = pk0;
+        p_out[64 + lane] = pk1;
+        if (g == 0) sum_lds[w][ln] = psum;
+
+        // V(j) has landed (K(j+1) may be in flight).
+        if (more) wait_vmcnt<NK>(); else wait_vmcnt<0>();
+        lds_barrier();
+
+        l_run = alpha * l_run + (sum_lds[2 * hb][ln] + sum_lds[2 * hb + 1][ln]);
+        m_run = m_new;
+
+        if (rescale) [[unlikely]] {
+#pragma unroll
+            for (int nt = 0; nt < NT; nt++) {
+                acc[nt] *= alpha;
+                __builtin_amdgcn_sched_barrier(0);  // one 16-register group at a time
+            }
+        }
+
+        // ---- values O^T += V^T P^T over the tile's four 16-key steps.
+        bf16x8 pop[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ks++) pop[ks] = ((const bf16x8 *)&xch_lds[2 * hb + (ks >> 1)][0][0])[64 * (ks & 1) + lane];
+        // Lane (g, ch, l16) addresses row 16ks + 8g + 4t2 + l16/4 and columns
+        // 32nt + 16ch + 4(l16%4) .. +3 of the wave's half of the slice; the
+        // transposing read returns column 32nt + 16ch + l16 of rows +0..3.
+        const int l16 = lane & 15;
+        const int ch = (lane >> 4) & 1;
+        const SA_LDS char *vrow = (const SA_LDS char *)v_lds + (8 * g + (l16 >> 2)) * VSTRIDE +
+                                  2 * (kb * NT * 32 + 16 * ch + 4 * (l16 & 3));
+        // Software-pipelined over the column groups: the four V^T operands of group
+        // nt+1 (eight transposing reads) are issued before the four MFMAs of group nt.
+        auto read_v = [&](int nt, bf16x8 (&vop)[4]) {
+#pragma unroll
+            for (int ks = 0; ks < 4; ks++) {
+#pragma unroll
+                for (int t2 = 0; t2 < 2; t2++) {
+                    const bf16x4 part = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                        (SA_LDS bf16x4 *)(vrow + (16 * ks + 4 * t2) * VSTRIDE + 64 * nt));
+                    vop[ks][4 * t2 + 0] = part[0];
+                    vop[ks][4 * t2 + 1] = part[1];
+                    vop[ks][4 * t2 + 2] = part[2];
+                    vop[ks][4 * t2 + 3] = part[3];
+                }
+            }
+        };
+        bf16x8 vcur[4], vnxt[4];
+        read_v(0, vcur);
 #pragma unroll
         for (int nt = 0; nt < NT; nt++) {
+            if (nt + 1 < NT) read_v(nt + 1, vnxt);
 #pragma unroll
-            for (int eq = 0; eq < 4; eq++) {
-                f32x4 o;
+            for (int ks = 0; ks < 4; ks++)
+                acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vcur[ks], pop[ks], acc[nt], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int i = 0; i < 4; i++) o[i] = bad ? inv_nan : acc[nt][4 * eq + i] / l_run;
-                *(f32x4 *)(orow + col0 + 32 * nt + 8 * eq + 4 * g) = o;
-            }
+            for (int ks = 0; ks < 4; ks++) vcur[ks] = vnxt[ks];
         }
+        lds_barrier();  // every wave is done with v_lds and the P operands
+
+        dma_idx(nx2, cur, j & 1);  // slot j&1 held item j's list, consumed above
+        if (more) dma_v(nx, iv_n);
+
+        if (last_of_unit) {
+            leave_unit(cur, bad);
+            if (more) enter_unit(nx);
+            // Outputs, query and sink of the next unit, and every gather issued so far
+            // complete here; the compiler sees nothing pending afterwards.
+            __builtin_amdgcn_s_waitcnt(0);
+            bad = bad_next;
+            bad_next = false;
+        }
+        cur = nx;
+        nx = nx2;
+        nx2 = next_item(nx2);
     }
+    wait_vmcnt<0>();
 }
 
 template <int HB, int NT>
-hipError_t launch_variant(const AttnArgs &a, int64_t grid, hipStream_t s) {
+hipError_t launch_variant(const AttnArgs &a, int64_t units, int64_t grid, hipStream_t s) {
     const int n_hg = (a.H + 32 * HB - 1) / (32 * HB);
-    hipLaunchKernelGGL((attn_bf16_kernel<HB, NT>), dim3((unsigned)grid), dim3(128 * HB), 0, s, a, n_hg);
+    hipLaunchKernelGGL((attn_bf16_kernel<HB, NT>), dim3((unsigned)grid), dim3(128 * HB), 0, s, a, n_hg, units);
     return hipGetLastError();
 }
 
@@ -449,38 +496,54 @@ AttnPlan plan_attn_bf16(int64_t rows, int H) {
     const int hb = H > 32 ? 2 : 1;
     p.heads_per_wg = 32 * hb;
     const int64_t n_hg = (H + p.heads_per_wg - 1) / p.heads_per_wg;
-    const int64_t units = rows * n_hg;
+    const int64_t rows_hg = rows * n_hg;
     // One workgroup per CU fits (the K tile alone is 64 KiB of LDS). With fewer
-    // (row, head block) units than CUs, column slices add workgroups; every slice
-    // gathers the full K tile but only its own V columns.
+    // (row, head block) pairs than CUs, column slices add units; every slice gathers
+    // the full K tile but only its own V columns.
     int nt = 8;
-    if (units < 64) nt = 1;
-    else if (units < 128) nt = 2;
-    else if (units < 256) nt = 4;
+    if (rows_hg < 64) nt = 1;
+    else if (rows_hg < 128) nt = 2;
+    else if (rows_hg < 256) nt = 4;
     p.cols_per_wg = 64 * nt;
-    p.grid = units * (kHeadDim / p.cols_per_wg);
+    p.units = rows_hg * (kHeadDim / p.cols_per_wg);
     p.threads = 128 * hb;
     p.lds_bytes = lds_bytes_of(hb, nt);
     return p;
 }
 
+namespace {
+// Compute units of the current device (cached per device): the persistent grid size,
+// since one workgroup of this kernel occupies a CU's LDS.
+int cu_count() {
+    static std::atomic<int> cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n > 0) return n;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+}  // namespace
+
 hipError_t launch_attn_bf16(const AttnArgs &a, hipStream_t s) {
     const AttnPlan p = plan_attn_bf16(a.rows, a.H);
-    if (p.grid == 0) return hipSuccess;
+    if (p.units == 0) return hipSuccess;
+    const int64_t grid = p.units < cu_count() ? p.units : cu_count();
     const int nt = p.cols_per_wg / 64;
     if (p.heads_per_wg == 64) {
         switch (nt) {
-            case 1: return launch_variant<2, 1>(a, p.grid, s);
-            case 2: return launch_variant<2, 2>(a, p.grid, s);
-            case 4: return launch_variant<2, 4>(a, p.grid, s);
-            default: return launch_variant<2, 8>(a, p.grid, s);
+            case 1: return launch_variant<2, 1>(a, p.units, grid, s);
+            case 2: return launch_variant<2, 2>(a, p.units, grid, s);
+            case 4: return launch_variant<2, 4>(a, p.units, grid, s);
+            default: return launch_variant<2, 8>(a, p.units, grid, s);
         }
     }
     switch (nt) {
-        case 1: return launch_variant<1, 1>(a, p.grid, s);
-        case 2: return launch_variant<1, 2>(a, p.grid, s);
-        case 4: return launch_variant<1, 4>(a, p.grid, s);
-        default: return launch_variant<1, 8>(a, p.grid, s);
+        case 1: return launch_variant<1, 1>(a, p.units, grid, s);
+        case 2: return launch_variant<1, 2>(a, p.units, grid, s);
+        case 4: return launch_variant<1, 4>(a, p.units, grid, s);
+        default: return launch_variant<1, 8>(a, p.units, grid, s);
     }
 }
 

@@ -47,7 +47,8 @@ hipError_t launch_unpad_heads(const float *out_pad, int64_t rows, int h_pad, int
 struct AttnPlan {
     int heads_per_wg;   // 32 or 64
     int cols_per_wg;    // 64, 128, 256 or 512
-    int64_t grid;       // workgroups
+    int64_t units;      // (row, head group, column slice) work units; the launch runs
+                        // min(units, compute units) persistent workgroups over them
     int threads;        // per workgroup
     int lds_bytes;      // static LDS per workgroup
 };
