@@ -54,4 +54,7 @@ struct AttnPlan {
 };
 AttnPlan plan_attn_bf16(int64_t rows, int H);
 
+// Compute units of the current device, cached per device (256 if the query fails).
+int device_cu_count();
+
 }  // namespace sa

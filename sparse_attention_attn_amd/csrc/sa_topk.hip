@@ -10,11 +10,11 @@
 // count is an integer, so the result is the unique exact answer.
 //
 // Two kernels find T:
-//   * topk_regs_kernel (rows of up to 32,768 scores): each lane keeps 32 or 64 keys
+//   * topk_regs_kernel (rows of up to 32,768 scores): each lane keeps 16 to 64 keys
 //     in registers; T is built bit by bit, from the top, as the largest value with
-//     at least k keys >= it (32 counting steps of v_cmp + ballot + popcount). Rows
-//     of up to 4,096 scores take one wave and no barrier at all; longer rows take 4
-//     or 16 waves that add their counts through LDS at each step.
+//     at least k keys >= it: a bisection over all keys until few enough share T's
+//     leading bits, then over those few alone. A row takes 1 to 8 waves; several
+//     waves add their counts through LDS.
 //   * topk_radix_kernel (longer rows): four 8-bit radix passes with LDS
 //     histograms, the keys cached in LDS when the row fits (32,768 scores) and
 //     re-read from memory otherwise.
@@ -37,6 +37,18 @@ __device__ __forceinline__ uint32_t order_key(float x) {
     u = u == 0x80000000u ? 0u : u;
     const uint32_t key = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
     return x != x ? 0u : key;
+}
+
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+
+// Per 16-bit half h of h2: 1 if h > c, else 0, for both halves of cx2 equal to c:
+// min(sat(h - c), 1) on packed unsigned 16-bit lanes (v_pk_sub_u16 with clamp, then
+// v_pk_min_u16). Written out because the compiler otherwise turns it into a compare and
+// select per half.
+__device__ __forceinline__ u16x2 ge_pair(uint32_t h2, uint32_t cx2, uint32_t one2) {
+    uint32_t t;
+    asm("v_pk_sub_u16 %0, %1, %2 clamp\n\tv_pk_min_u16 %0, %0, %3" : "=&v"(t) : "v"(h2), "s"(cx2), "s"(one2));
+    return __builtin_bit_cast(u16x2, t);
 }
 
 __device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
@@ -153,13 +165,43 @@ __global__ void __launch_bounds__(kThreads) topk_radix_kernel(TopkArgs a) {
 }
 
 
+// Sum over the wave of a per-lane count: DPP row shifts build each 16-lane row's
+// inclusive sum, the two row broadcasts carry rows 0 and 0..1 upward, and lane 63
+// ends with the total.
+__device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, false);  // row_shr:1
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, false);  // row_shr:2
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, false);  // row_shr:4
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, false);  // row_shr:8
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false);  // row_bcast:31
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
 // WAVES waves per row, KPL keys per lane: a wave covers 64 * KPL positions.
+//
+// The threshold T (the k-th largest key) is the largest value with at least k keys
+// at or above it. It is found in two phases that keep the bracket lo <= T < hi,
+// hi = lo + 2^b, with c_lo / c_hi the numbers of keys at or above lo / hi:
+//   coarse: bisection over every key, one bit per step from the top, each step a
+//     per-lane count (compare + add) summed over the row; it stops as soon as at
+//     most kCand keys fall inside the bracket;
+//   fine: those keys (sharing T's upper bits) are compacted through LDS, every wave
+//     loads all of them (at most four per lane), and the remaining bits are decided
+//     over them alone, plus the fixed count of keys above the bracket it started from.
+// At the end hi = T + 1, so c_hi keys are > T and c_lo - c_hi equal T; when all ties
+// are taken (the usual case), the selection is simply key >= T.
 template <int WAVES, int KPL>
 __global__ void __launch_bounds__(64 * WAVES) topk_regs_kernel(TopkArgs a) {
-    constexpr int kKeysPerLane = KPL;
+    static_assert(KPL % 4 == 0, "keys per lane pair up twice in the packed count");
     constexpr int kWaveSpan = 64 * KPL;
+    constexpr int kCandPerLane = 4;
+    constexpr uint32_t kCand = 64 * kCandPerLane;
     __shared__ uint32_t cnt_lds[2][WAVES];
-    __shared__ uint32_t tot_lds[2][WAVES];
+    __shared__ uint32_t tot_lds[WAVES];
+    constexpr int kStage = 4096;
+    __shared__ uint32_t cand_lds[kCand + 64];
+    __shared__ int32_t out_lds[kStage + 64];
 
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -184,23 +226,18 @@ __global__ void __launch_bounds__(64 * WAVES) topk_regs_kernel(TopkArgs a) {
     // vl > k >= 1) so that all of them are in flight together; the key is masked after.
     // live(p) = all ones when p < vl, else 0 (arithmetic, so no per-key branch).
     auto live = [&](int p) -> uint32_t { return (uint32_t)((p - vl) >> 31); };
-    float x[kKeysPerLane];
+    float x[KPL];
 #pragma unroll
-    for (int r = 0; r < kKeysPerLane; r++) {
+    for (int r = 0; r < KPL; r++) {
         const int p = base + 64 * r;
         x[r] = srow[p & (int)live(p)];
     }
-    uint32_t key[kKeysPerLane];
+    uint32_t key[KPL];
 #pragma unroll
-    for (int r = 0; r < kKeysPerLane; r++) key[r] = order_key(x[r]) & live(base + 64 * r);
+    for (int r = 0; r < KPL; r++) key[r] = order_key(x[r]) & live(base + 64 * r);
 
-    auto wave_count = [&](auto pred) -> uint32_t {
-        uint32_t c = 0u;
-#pragma unroll
-        for (int r = 0; r < kKeysPerLane; r++) c += (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(pred(r)));
-        return c;
-    };
-    // Sum of one count per wave, in wave order; slot alternates so one barrier suffices.
+    // Row-wide sum of one per-wave value, in wave order; the slot alternates so that one
+    // barrier per call suffices.
     auto row_total = [&](uint32_t c, int slot) -> uint32_t {
         if constexpr (WAVES == 1) {
             return c;
@@ -214,45 +251,149 @@ __global__ void __launch_bounds__(64 * WAVES) topk_regs_kernel(TopkArgs a) {
         }
     };
 
-    // T = the k-th largest key: the largest value with at least k keys >= it.
-    uint32_t T = 0u;
-    for (int bit = 31; bit >= 0; bit--) {
-        const uint32_t cand = T | (1u << bit);
-        const uint32_t c = row_total(wave_count([&](int r) { return key[r] >= cand; }), bit & 1);
-        if (c >= k) T = cand;
-    }
-
-    // Counts above T and equal to T (within the row) per wave, then each wave's offsets.
-    const uint32_t gt_w = wave_count([&](int r) { return key[r] > T; });
-    const uint32_t eq_w = wave_count([&](int r) { return key[r] == T && base + 64 * r < vl; });
-    uint32_t gt_before = 0u, gt_all = gt_w, eq_before = 0u;
-    if constexpr (WAVES > 1) {
-        if (lane == 0) { cnt_lds[0][w] = gt_w; tot_lds[0][w] = eq_w; }
-        __syncthreads();
-        gt_all = 0u;
+    // ---- coarse phase. Every tested value is >= 1, so the zero keys past the row never
+    // count; NaN keys (also 0) count only towards c_lo = vl at the start.
+    uint32_t lo = 0u, c_lo = (uint32_t)vl, c_hi = 0u;
+    int bit = 32;  // the bracket is [lo, lo + 2^bit)
+    {
+        // While the tested bit is 16 or higher, the candidate's low half is zero, so
+        // key >= cand compares the upper halves only: two keys per register, counted by
+        // min(sat(h - (c - 1)), 1) on packed 16-bit lanes (1 iff h >= c), no lane masks.
+        uint32_t hk[KPL / 2];
 #pragma unroll
-        for (int ww = 0; ww < WAVES; ww++) {
-            const uint32_t g = cnt_lds[0][ww], e = tot_lds[0][ww];
-            gt_all += g;
-            gt_before += ww < w ? g : 0u;
-            eq_before += ww < w ? e : 0u;
+        for (int i = 0; i < KPL / 2; i++) hk[i] = (key[2 * i] >> 16) | (key[2 * i + 1] & 0xffff0000u);
+        const uint32_t one2 = 0x00010001u;
+        while (bit > 16 && c_lo - c_hi > kCand) {
+            bit--;
+            const uint32_t cand = lo | (1u << bit);
+            const uint32_t cm1 = (cand >> 16) - 1u;
+            const uint32_t cm1x2 = cm1 | (cm1 << 16);
+            u16x2 acc0 = (u16x2){0, 0}, acc1 = (u16x2){0, 0};  // two chains in flight
+#pragma unroll
+            for (int i = 0; i < KPL / 2; i += 2) {
+                acc0 += ge_pair(hk[i], cm1x2, one2);
+                acc1 += ge_pair(hk[i + 1], cm1x2, one2);
+            }
+            const u16x2 acc = acc0 + acc1;
+            uint32_t c = (uint32_t)acc[0] + (uint32_t)acc[1];
+            c = row_total(wave_sum(c), bit & 1);
+            if (c >= k) { lo = cand; c_lo = c; } else { c_hi = c; }
         }
     }
-    const uint32_t need = k - gt_all;  // keys equal to T to take, lowest positions first
-    // Selected before this wave: every key > T there, and its share of the first `need` ties.
-    uint32_t sel_base = gt_before + (eq_before < need ? eq_before : need);
-    uint32_t eq_base = eq_before;
+    while (bit > 0 && c_lo - c_hi > kCand) {
+        bit--;
+        const uint32_t cand = lo | (1u << bit);
+        uint32_t c = 0u;
 #pragma unroll
-    for (int r = 0; r < kKeysPerLane; r++) {
-        const int p = base + 64 * r;
-        const bool eq = key[r] == T && p < vl;
-        const uint64_t meq = __builtin_amdgcn_ballot_w64(eq);
-        const bool sel = key[r] > T || (eq && eq_base + lanes_below(meq) < need);
-        const uint64_t msel = __builtin_amdgcn_ballot_w64(sel);
-        const uint32_t pos = sel_base + lanes_below(msel);
-        if (sel && pos < k) orow[pos] = p;  // exactly k are selected; the bound is a guard
-        eq_base += (uint32_t)__builtin_popcountll(meq);
-        sel_base += (uint32_t)__builtin_popcountll(msel);
+        for (int r = 0; r < KPL; r++) c += key[r] >= cand ? 1u : 0u;
+        c = row_total(wave_sum(c), bit & 1);
+        if (c >= k) { lo = cand; c_lo = c; } else { c_hi = c; }
+    }
+
+    // ---- fine phase over the keys inside the bracket (at most kCand of them).
+    // Per-key predicates are combined with & (not &&) and every LDS write is issued, to a
+    // spare slot per lane when the key is not taken, so these loops have no branches.
+    if (bit > 0) {
+        const uint32_t span_m1 = bit >= 32 ? 0xffffffffu : (1u << bit) - 1u;
+        auto inside = [&](int r) { return (key[r] - lo <= span_m1) & (base + 64 * r < vl); };
+        uint32_t before = 0u;
+        if constexpr (WAVES > 1) {
+            uint32_t mine = 0u;
+#pragma unroll
+            for (int r = 0; r < KPL; r++) mine += (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(inside(r)));
+            if (lane == 0) tot_lds[w] = mine;
+            __syncthreads();
+#pragma unroll
+            for (int ww = 0; ww < WAVES; ww++) before += ww < w ? tot_lds[ww] : 0u;
+        }
+#pragma unroll
+        for (int r = 0; r < KPL; r++) {
+            const bool in = inside(r);
+            const uint64_t m = __builtin_amdgcn_ballot_w64(in);
+            const uint32_t j = before + lanes_below(m);
+            // exactly c_lo - c_hi keys are inside; the bound is a guard
+            cand_lds[(in & (j < kCand)) ? j : kCand + lane] = key[r];
+            before += (uint32_t)__builtin_popcountll(m);
+        }
+        __syncthreads();
+        const uint32_t ncand = c_lo - c_hi;
+        uint32_t ck[kCandPerLane];
+#pragma unroll
+        for (int i = 0; i < kCandPerLane; i++) {
+            const uint32_t j = 64u * i + lane;
+            ck[i] = j < ncand ? cand_lds[j] : 0u;
+        }
+        const uint32_t c_above = c_hi;  // keys >= the bracket's upper end at entry
+        while (bit > 0) {
+            bit--;
+            const uint32_t cand = lo | (1u << bit);
+            uint32_t c = c_above;
+#pragma unroll
+            for (int i = 0; i < kCandPerLane; i++)
+                c += (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(ck[i] >= cand));
+            if (c >= k) { lo = cand; c_lo = c; } else { c_hi = c; }
+        }
+    }
+    const uint32_t T = lo;
+    const uint32_t need = k - c_hi;           // keys equal to T to take, lowest positions first
+    const bool all_ties = need == c_lo - c_hi;
+
+    // ---- ordered selection. Selected before this wave: every key > T there, and its
+    // share of the first `need` ties.
+    uint32_t sel_base = 0u, eq_base = 0u;
+    if constexpr (WAVES > 1) {
+        __syncthreads();  // every wave has read the last coarse totals from cnt_lds
+        uint32_t gt_w = 0u, eq_w = 0u;
+#pragma unroll
+        for (int r = 0; r < KPL; r++) {
+            gt_w += (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(key[r] > T));
+            eq_w += (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64((key[r] == T) & (base + 64 * r < vl)));
+        }
+        if (lane == 0) { cnt_lds[0][w] = gt_w; cnt_lds[1][w] = eq_w; }
+        __syncthreads();
+        uint32_t gt_before = 0u;
+#pragma unroll
+        for (int ww = 0; ww < WAVES; ww++) {
+            gt_before += ww < w ? cnt_lds[0][ww] : 0u;
+            eq_base += ww < w ? cnt_lds[1][ww] : 0u;
+        }
+        sel_base = gt_before + (eq_base < need ? eq_base : need);
+    }
+    // Selected positions go to out_lds[pos] (a spare slot per lane otherwise) when the
+    // output row fits there, and leave in coalesced stores; else straight to memory.
+    const bool staged = k <= (uint32_t)kStage;
+    auto emit = [&](bool sel, uint32_t pos, int p) {
+        if (staged) {
+            out_lds[(sel & (pos < k)) ? pos : kStage + lane] = p;
+        } else if (sel && pos < k) {  // exactly k are selected; the bound is a guard
+            orow[pos] = p;
+        }
+    };
+    if (all_ties) {
+#pragma unroll
+        for (int r = 0; r < KPL; r++) {
+            const int p = base + 64 * r;
+            const bool sel = (key[r] >= T) & (p < vl);
+            const uint64_t msel = __builtin_amdgcn_ballot_w64(sel);
+            emit(sel, sel_base + lanes_below(msel), p);
+            sel_base += (uint32_t)__builtin_popcountll(msel);
+        }
+    } else {
+#pragma unroll
+        for (int r = 0; r < KPL; r++) {
+            const int p = base + 64 * r;
+            const bool eq = (key[r] == T) & (p < vl);
+            const uint64_t meq = __builtin_amdgcn_ballot_w64(eq);
+            const bool sel = (key[r] > T) | (eq & (eq_base + lanes_below(meq) < need));
+            const uint64_t msel = __builtin_amdgcn_ballot_w64(sel);
+            emit(sel, sel_base + lanes_below(msel), p);
+            eq_base += (uint32_t)__builtin_popcountll(meq);
+            sel_base += (uint32_t)__builtin_popcountll(msel);
+        }
+    }
+    if (staged) {
+        __syncthreads();
+        for (int i = threadIdx.x; i < (int)k; i += 64 * WAVES) orow[i] = out_lds[i];
     }
     if (threadIdx.x == 0 && a.count_out) a.count_out[row] = (int32_t)k;
 }
@@ -263,11 +404,16 @@ hipError_t launch_topk(const TopkArgs &a, hipStream_t s) {
     if (a.rows == 0) return hipSuccess;
     const dim3 grid((unsigned)a.rows);
     if (a.n <= 64 * 64) {
-        hipLaunchKernelGGL((topk_regs_kernel<1, 64>), grid, dim3(64), 0, s, a);
+        // One wave per row has the most rows in flight; with at most four rows per CU,
+        // four waves per row shorten each row's chain of dependent steps instead.
+        if (a.rows <= 4 * (int64_t)device_cu_count())
+            hipLaunchKernelGGL((topk_regs_kernel<4, 16>), grid, dim3(256), 0, s, a);
+        else
+            hipLaunchKernelGGL((topk_regs_kernel<1, 64>), grid, dim3(64), 0, s, a);
     } else if (a.n <= 4 * 64 * 64) {
         hipLaunchKernelGGL((topk_regs_kernel<4, 64>), grid, dim3(256), 0, s, a);
-    } else if (a.n <= 16 * 64 * 32) {
-        hipLaunchKernelGGL((topk_regs_kernel<16, 32>), grid, dim3(1024), 0, s, a);
+    } else if (a.n <= 8 * 64 * 64) {
+        hipLaunchKernelGGL((topk_regs_kernel<8, 64>), grid, dim3(512), 0, s, a);
     } else {
         hipLaunchKernelGGL(topk_radix_kernel, grid, dim3(kThreads), 0, s, a);
     }

@@ -95,3 +95,29 @@ def test_mid_rows_four_waves():
     s[2, 5000:7000] = 0.25
     check(s, 640, np.array([10000, 4097, 6500, 700, 9999], np.int32), label="n=10000")
     check(np.round(s * 8) / 8, 1000, label="n=10000 ties")
+
+
+def test_decode_shape():
+    """The decode step's selection: 1,024 rows x 4,096 N(0,1) scores, top-640 (several
+    waves per row), plus the same rows rounded to 1/8 (many ties at the threshold)."""
+    rng = np.random.default_rng(75)
+    s = rng.standard_normal((1024, 4096)).astype(np.float32)
+    check(s, 640, label="decode 1024x4096")
+    check(np.round(s * 8) / 8, 640, label="decode 1024x4096 ties")
+
+
+def test_shared_upper_bits():
+    """More than 256 keys agree in their upper 16 bits, so the bisection over every key
+    continues into the lower half before the few remaining ones are singled out."""
+    rng = np.random.default_rng(76)
+    for rows, n in ((4, 4096), (1500, 4096), (2, 12000)):
+        s = (1.0 + rng.integers(0, 1 << 14, size=(rows, n)) * 2.0 ** -22).astype(np.float32)
+        check(s, 640, label=f"shared upper bits {rows}x{n}")
+
+
+def test_large_k_unstaged():
+    """k above 4,096: selected positions are written straight to memory."""
+    rng = np.random.default_rng(77)
+    s = rng.standard_normal((3, 20000)).astype(np.float32)
+    s[1, ::7] = 0.5
+    check(s, 5000, label="k=5000")
