@@ -74,7 +74,7 @@ def cpu_baseline(inp, scores, out_gpu, idx_gpu, heads, k, budget_s: float, max_r
 
     The oracle's results for those rows are also compared with what the timed GPU
     launch produced for them (indices bit-exact; attention within the bf16 tolerance
-    |g - o| <= 2e-3 + 1e-2 |o| with equal nonfinite classes)."""
+    max |g - o| <= 2e-3 over finite elements, with equal nonfinite classes)."""
     import numpy as np
 
     import oracle
@@ -99,7 +99,7 @@ def cpu_baseline(inp, scores, out_gpu, idx_gpu, heads, k, budget_s: float, max_r
         ok &= bool(np.array_equal(idx[0], idx_host[r]))
         ok &= bool(np.array_equal(np.isnan(g), np.isnan(o)) and np.array_equal(np.isinf(g), np.isinf(o)))
         err = np.abs(g[fin] - o[fin])
-        ok &= bool(np.all(err <= 2e-3 + 1e-2 * np.abs(o[fin])))
+        ok &= bool(np.all(err <= 2e-3))
         max_err = max(max_err, float(err.max()) if err.size else 0.0)
         rows_done += 1
     value = rows_done * heads / t_total

@@ -44,119 +44,11 @@
 
 #include <atomic>
 
+#include "sa_device.h"
 #include "sa_internal.h"
 
 namespace sa {
 namespace {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-
-#define SA_LDS __attribute__((address_space(3)))
-
-constexpr int kHeadDim = 512;   // sixteen 32-wide output column groups
-constexpr int kTile = 64;       // keys per online-softmax tile
-constexpr int kRowBytes = kHeadDim * 2;
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLazy = 8.0f;  // log2 units: p <= 256 between reference moves
-constexpr int kQLoads = 17;      // per wave: sixteen 16-byte query pieces and one sink
-// Word 3 of a raw buffer resource (32-bit data format, no swizzle) and an offset past any
-// output row (stores there are dropped by the buffer range check).
-constexpr int kBufferFlags = 0x00020000;
-constexpr int kDropOffset = 0x7ffffff0;
-// Cache policy of the output stores: non-temporal. The outputs are never read back by
-// the kernel, and streaming them keeps them from contending with the gathers in the
-// caches (a 12% shorter decode step at 1,024 rows, measured).
-constexpr int kStoreNT = 2;
-// s_waitcnt vmcnt holds at most 63: a larger count is clamped, which waits longer.
-constexpr int vm_clamp(int n) { return n > 63 ? 63 : n; }
-
-// 2^x on the hardware exponential (v_exp_f32); exp2(-inf) = 0, exp2(+inf) = inf, NaN stays NaN.
-__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// Source of the DMA for keys that are masked or invalid: 1 KiB of zeros.
-__device__ __attribute__((aligned(16))) const uint32_t g_zero_row[kRowBytes / 4] = {0};
-
-// All vector-memory traffic inside the tile loop is issued through the asm helpers
-// below, so the compiler neither sees nor waits on it: the loop's only waits on the
-// vector-memory counter are the explicit ones, each placed where one tile's
-// gathers must have landed while the next tile's stay in flight.
-
-// s_waitcnt vmcnt(N): this wave has at most N vector-memory operations outstanding.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
-// Workgroup barrier for LDS traffic only: outstanding LDS operations complete,
-// in-flight DMA gathers stay in flight.
-__device__ __forceinline__ void lds_barrier() {
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const void *p) {
-    return (uint32_t)(uintptr_t)(const SA_LDS void *)p;
-}
-
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-// Direct-to-LDS gather: lane i moves 16 bytes from sbase + voff_i to LDS address
-// lds + 16 i (M0 holds the wave's LDS base). sbase and lds are wave-uniform. The load is
-// non-temporal: a gathered cache row is used once per query row, and keeping the stream
-// out of the caches' retained set measured 8% faster at 1,024 rows.
-__device__ __forceinline__ void dma16(const void *sbase, uint32_t voff, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 nt"
-                 ::"s"(lds), "v"(voff), "s"(sbase) : "memory", "m0");
-}
-// Same with 4 bytes per lane (LDS address lds + 4 i).
-__device__ __forceinline__ void dma4(const void *sbase, uint32_t voff, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
-                 ::"s"(lds), "v"(voff), "s"(sbase) : "memory", "m0");
-}
-// Asynchronous loads into registers: the destination is written when the data
-// returns, which the compiler does not model, so the value may be used only after an
-// explicit vector-memory wait that covers the load, followed by register_ready on it.
-__device__ __forceinline__ void load16_async(bf16x8 &dst, const void *p) {
-    asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(dst) : "v"(p) : "memory");
-}
-__device__ __forceinline__ void load4_async(float &dst, const void *p) {
-    asm volatile("global_load_dword %0, %1, off" : "=v"(dst) : "v"(p) : "memory");
-}
-#pragma clang diagnostic pop
-// Orders every later use of v after the preceding (volatile) wait.
-template <typename T>
-__device__ __forceinline__ void register_ready(T &v) {
-    asm volatile("" : "+v"(v));
-}
-
-// Bits 2 and 3 of m exchanged. Row m of a 32-key MFMA block holds key pi(m), which
-// makes each lane's sixteen scores two runs of eight consecutive keys (the P operand).
-__device__ __forceinline__ int swap23(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
-
-// LDS row strides. A K row is padded by 16 bytes: the 16 lanes of one ds_read_b128
-// read 16 consecutive slots at the same column and land on 16 different 16-byte
-// bank groups. A V row is padded by 64 bytes: one ds_read_b64_tr_b16 reads rows
-// {0..3} + 8g of a 16-key step at a 64-byte column window, and with a stride of
-// 64 (mod 256) bytes every 4-byte bank is hit exactly twice by its 512 bytes.
-// Either way each read is one base register plus an immediate offset.
-constexpr int kKStride = kRowBytes + 16;
-
-// K slot s holds tile key (s & 32) | swap23(s & 31), so MFMA row m of key block kb
-// (which must hold key kb*32 + swap23(m)) reads slot kb*32 + m.
-__device__ __forceinline__ int key_of_slot(int s) { return (s & 32) | swap23(s & 31); }
-
-// Map the linear workgroup id so that the workgroups of one query row (its head
-// groups and column slices, which gather the same cache rows) run on one XCD and
-// share its L2. Dispatch places workgroup i on XCD i % 8.
-__device__ __forceinline__ int64_t xcd_remap(int64_t i, int64_t G) {
-    const int64_t xcd = i & 7, slot = i >> 3;
-    const int64_t per = G >> 3, rem = G & 7;
-    return xcd * per + (xcd < rem ? xcd : rem) + slot;
-}
 
 // Kernel template.
 //   HB: head blocks of 32 per workgroup (1 or 2); the workgroup has 2*HB waves.
@@ -468,18 +360,33 @@ attn_bf16_kernel(AttnArgs a, int n_hg, int64_t units) {
             alpha = exp2_hw(ref - ref_new);
             ref = ref_new;
         }
-        bf16x8 pk0, pk1;
+        // p = hi + lo with both parts bf16, so the value product (one MFMA per part) sees
+        // p to about 16 significant bits and l sums the same hi + lo. For p > 0 both parts
+        // are positive, so an infinite value times a positive weight stays infinite (never
+        // inf - inf or 0 * inf): hi is p truncated toward zero and lo = bf16(p - hi); when
+        // p is itself a bf16 value, hi is the next bf16 below it and lo its last unit, so
+        // hi + lo = p exactly (exact sums stay exact).
+        bf16x8 ph0, ph1, pl0, pl1;
         float psum = 0.0f;
 #pragma unroll
         for (int e = 0; e < 16; e++) {
-            const __bf16 pb = (__bf16)exp2_hw(s[e] - ref);
-            psum += (float)pb;
-            if (e < 8) pk0[e] = pb; else pk1[e - 8] = pb;
+            const float pf = exp2_hw(s[e] - ref);
+            const uint32_t pbits = __float_as_uint(pf);
+            const uint32_t trunc = pbits >> 16;
+            const bool exact = (pbits & 0xffffu) == 0u && pf > 0.0f;
+            const uint32_t hb = pf != pf ? 0x7fc0u : (exact ? trunc - 1u : trunc);
+            const float hif = __uint_as_float(hb << 16);
+            const __bf16 hi = __builtin_bit_cast(__bf16, (uint16_t)hb);
+            const __bf16 lo = (__bf16)(pf - hif);
+            psum += hif + (float)lo;
+            if (e < 8) { ph0[e] = hi; pl0[e] = lo; } else { ph1[e - 8] = hi; pl1[e - 8] = lo; }
         }
         psum += __shfl_xor(psum, 32);
         bf16x8 *p_out = (bf16x8 *)&xch_lds[w][0][0];
-        p_out[lane] = pk0;
-        p_out[64 + lane] = pk1;
+        p_out[lane] = ph0;
+        p_out[64 + lane] = ph1;
+        p_out[128 + lane] = pl0;
+        p_out[192 + lane] = pl1;
         if (g == 0) sum_lds[w][ln] = psum;
 
         // V(j) has landed (stores, K(j+1) and a query may be in flight).
@@ -504,9 +411,13 @@ attn_bf16_kernel(AttnArgs a, int n_hg, int64_t units) {
         }
 
         // ---- values O^T += V^T P^T over the tile's four 16-key steps.
-        bf16x8 pop[4];
+        bf16x8 pop[4], pol[4];  // hi and lo parts of P
 #pragma unroll
-        for (int ks = 0; ks < 4; ks++) pop[ks] = ((const bf16x8 *)&xch_lds[2 * hb + (ks >> 1)][0][0])[64 * (ks & 1) + lane];
+        for (int ks = 0; ks < 4; ks++) {
+            const bf16x8 *src = (const bf16x8 *)&xch_lds[2 * hb + (ks >> 1)][0][0];
+            pop[ks] = src[64 * (ks & 1) + lane];
+            pol[ks] = src[128 + 64 * (ks & 1) + lane];
+        }
         // Lane (g, ch, l16) addresses row 16ks + 8g + 4t2 + l16/4 and columns
         // 32nt + 16ch + 4(l16%4) .. +3 of the wave's half of the slice; the
         // transposing read returns column 32nt + 16ch + l16 of rows +0..3.
@@ -536,8 +447,10 @@ attn_bf16_kernel(AttnArgs a, int n_hg, int64_t units) {
         for (int nt = 0; nt < NT; nt++) {
             if (nt + 1 < NT) read_v(nt + 1, vnxt);
 #pragma unroll
-            for (int ks = 0; ks < 4; ks++)
+            for (int ks = 0; ks < 4; ks++) {
                 acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vcur[ks], pop[ks], acc[nt], 0, 0, 0);
+                acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vcur[ks], pol[ks], acc[nt], 0, 0, 0);
+            }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int ks = 0; ks < 4; ks++) vcur[ks] = vnxt[ks];

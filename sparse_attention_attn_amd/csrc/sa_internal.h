@@ -35,6 +35,9 @@ struct TopkArgs {
 
 // Enqueue helpers; they assume validated arguments and return the HIP launch status.
 hipError_t launch_attn_bf16(const AttnArgs &a, hipStream_t s);
+// The same operation when a.k == a.v (one cache serving as keys and values): each
+// selected row is gathered once.
+hipError_t launch_attn_bf16_alias(const AttnArgs &a, hipStream_t s);
 hipError_t launch_attn_f32(const AttnArgs &a, hipStream_t s);
 hipError_t launch_topk(const TopkArgs &a, hipStream_t s);
 hipError_t launch_pad_heads(int dtype, const void *q, int64_t rows, int h_real, int h_pad,

@@ -1,10 +1,10 @@
 """Comparison of GPU outputs against the float64 oracle, and host<->device plumbing.
 
-Bar: nonfinite classes (NaN, +inf, -inf, finite) must match element by element;
-finite elements must satisfy |gpu - oracle| <= atol + rtol * |oracle| with
-(atol, rtol) = (2e-3, 1e-2) for bf16 inputs and (1e-5, 1e-5) for float32 inputs.
-The allclose form is used because outputs near zero make a pure relative bound
-meaningless; max abs and max rel errors are reported separately.
+Bar: nonfinite classes (NaN, +inf, -inf, finite) must match element by element, and
+every finite element must satisfy |gpu - oracle| <= atol: the maximum absolute error
+is 2e-3 for bf16 inputs and 1e-5 for float32 inputs. For bf16 this also bounds the
+relative error by 1e-2 wherever |oracle| >= 0.2; below that a relative bound is not
+meaningful (outputs cancel towards zero), so max rel error is reported, not imposed.
 """
 from __future__ import annotations
 
@@ -38,7 +38,9 @@ def assert_parity(gpu, ref, atol: float, rtol: float, label: str = "") -> dict:
     stats = {"n": int(fin.sum()), "nonfinite": int((~fin).sum()),
              "max_abs": float(err.max()) if err.size else 0.0,
              "max_rel": float((err / np.maximum(np.abs(o), 1e-30)).max()) if err.size else 0.0}
-    bad = err > atol + rtol * np.abs(o)
+    bad = err > atol
+    big = np.abs(o) >= atol / rtol
+    stats["max_rel_where_large"] = float((err[big] / np.abs(o[big])).max()) if big.any() else 0.0
     if bad.any():
         idx = np.flatnonzero(fin)[np.flatnonzero(bad)[0]]
         at = np.unravel_index(idx, gpu.shape)

@@ -285,3 +285,16 @@ def test_sustained_decode_sampled():
         assert_parity(out[r:r + 1].cpu().numpy(), ref, *BF16_TOL, f"sustained row {r}")
     del inp
     torch.cuda.empty_cache()
+
+
+def test_few_keys_precision():
+    """Rows that select only a few keys of comparable weight: the value sum cancels
+    towards zero while each term is large, so the weights p must enter the value product
+    with more than bf16's 8 bits (they go in as a hi + lo pair of bf16 parts)."""
+    rng = np.random.default_rng(95)
+    c = w.decode_bf16(seed=95, batch=64, heads=64, n_ctx=300, k=40, name="few keys")
+    c.nsel[:] = rng.integers(1, 41, size=64).astype(np.int32)
+    got, ref = check_case(c, label="few keys")
+    err = np.abs(got.astype(np.float64) - ref)
+    say(f"  max abs error {err.max():.2e}")
+    assert err.max() < 1e-4
