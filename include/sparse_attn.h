@@ -71,6 +71,9 @@ extern "C" {
 #define SA_HEAD_DIM 512
 /* Largest number of heads one call accepts. */
 #define SA_MAX_HEADS 128
+/* Largest n_ctx (cache positions) of a bf16 call: 4 GiB of cache per 1 KiB position row.
+   Larger bf16 caches are refused with SA_ERR_UNSUPPORTED. */
+#define SA_BF16_MAX_CTX 4194303
 
 /* Returns SA_ABI_VERSION of the loaded library. */
 int sparse_attn_abi_version(void);
@@ -101,7 +104,8 @@ size_t sparse_attn_workspace_bytes(int op, int64_t rows, int32_t heads, int32_t 
  *   sinks     [H] float32 per-head sink logits
  *   scale     multiplies q.k (not the sinks)
  *   out       [B, H, D] float32
- * Requires D == 512, 1 <= H <= 128, B >= 0, kmax >= 1, n_ctx >= 1.
+ * Requires D == 512, 1 <= H <= 128, B >= 0, kmax >= 1, n_ctx >= 1
+ * (n_ctx <= SA_BF16_MAX_CTX for SA_BF16).
  */
 int sparse_attn_decode(int dtype, const void *q, const void *k_cache, const void *v_cache,
                        int64_t n_ctx, const int32_t *idx, const int32_t *nsel, int32_t kmax,

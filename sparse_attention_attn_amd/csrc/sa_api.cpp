@@ -71,6 +71,10 @@ int check_attn(int dtype, const void *q, const void *k, const void *v, int64_t n
     if (!aligned(idx, 4) || !aligned(sinks, 4) || (nsel && !aligned(nsel, 4)))
         return fail(SA_ERR_UNSUPPORTED, "idx, nsel and sinks must be 4-byte aligned");
     if (dtype == SA_BF16) {
+        // The gathers address a cache through a 32-bit byte range (1 KiB per position).
+        if (n_ctx > SA_BF16_MAX_CTX)
+            return fail(SA_ERR_UNSUPPORTED, "n_ctx %lld: bf16 caches hold at most %d positions", (long long)n_ctx,
+                        SA_BF16_MAX_CTX);
         const sa::AttnPlan p = sa::plan_attn_bf16(rows, H);
         if (p.units > kMaxGrid) return fail(SA_ERR_SHAPE, "too many rows for one launch");
     } else if ((int64_t)rows * H > kMaxGrid) {

@@ -145,27 +145,30 @@ attn_bf16_kernel(AttnArgs a, int n_hg, int64_t units) {
         if (__builtin_amdgcn_ballot_w64(live && !inr)) bad = true;
         return (live && inr) ? iv : -1;
     };
-    // One DMA instruction gathers one cache row (64 lanes x 16 bytes = 1 KiB) into
-    // an LDS slot; lane i moves bytes [16i, 16i + 16) of the row.
+    // One DMA instruction gathers one cache row (64 lanes x 16 bytes = 1 KiB) into an
+    // LDS slot; lane i moves bytes [16i, 16i + 16) of the row. Wave w gathers keys
+    // NK*w + i. The buffer resource spans the row's cache; a masked key (-1) has a
+    // wrapped-around offset past its end and arrives as zeros.
     auto dma_k = [&](const Item &it, int iv) {
-        const char *kbase = kbase_of(it);
+        const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)kbase_of(it), 0, (int)(uint32_t)(a.n_ctx * kRowBytes), kBufferFlags);
+        SA_LDS char *kw = (SA_LDS char *)k_lds + (NK * w) * kKStride;
 #pragma unroll
         for (int i = 0; i < NK; i++) {
-            const int slot = w * NK + i;
-            const int ij = __builtin_amdgcn_readlane(iv, key_of_slot(slot));
-            const char *rbase = ij >= 0 ? kbase + (int64_t)ij * kRowBytes : (const char *)g_zero_row;
-            dma16(rbase, (uint32_t)lane << 4, lds_addr(k_lds + slot * kKStride));
+            const int ij = __builtin_amdgcn_readlane(iv, NK * w + i);
+            dma16_buf(rsrc, ((uint32_t)ij << 10) + ((uint32_t)lane << 4), lds_addr(kw + swap23(i) * kKStride));
         }
     };
     // V rows keep the tile's key order; only the unit's column slice is moved.
     auto dma_v = [&](const Item &it, int iv) {
-        const char *vbase = vbase_of(it);
+        const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)vbase_of(it), 0, (int)(uint32_t)(a.n_ctx * kRowBytes - (int64_t)it.cs * VROW), kBufferFlags);
 #pragma unroll
         for (int i = 0; i < NV; i++) {
             const int j = w * NV + i;
             const int ij = __builtin_amdgcn_readlane(iv, j);
-            const char *rbase = ij >= 0 ? vbase + (int64_t)ij * kRowBytes : (const char *)g_zero_row;
-            if (VCHUNKS == 64 || lane < VCHUNKS) dma16(rbase, (uint32_t)lane << 4, lds_addr(v_lds + j * VSTRIDE));
+            if (VCHUNKS == 64 || lane < VCHUNKS)
+                dma16_buf(rsrc, ((uint32_t)ij << 10) + ((uint32_t)lane << 4), lds_addr(v_lds + j * VSTRIDE));
         }
     };
 

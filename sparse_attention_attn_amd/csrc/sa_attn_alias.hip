@@ -138,16 +138,19 @@ attn_bf16_alias_kernel(AttnArgs a, int n_hg, int64_t units) {
         }
         return (live && inr) ? iv : -1;
     };
-    // One DMA instruction per cache row (1 KiB) into slot s = w*NR + i of buffer buf,
-    // which holds key key_of_slot(s). Always NR instructions: with no item, zero rows.
+    // One DMA instruction per cache row (1 KiB): wave w gathers keys NR*w + i into slots
+    // NR*w + swap23(i) of buffer buf. The buffer resource spans the row's cache; a masked
+    // key (-1) has a wrapped-around offset past its end and arrives as zeros, and so does
+    // every row when there is no item (the resource is then empty).
     auto dma_tile = [&](const Item &it, int iv, int buf) {
-        const char *cbase = it.unit >= 0 ? (const char *)a.k + it.row * a.cache_stride * 2 : (const char *)g_zero_row;
+        const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)((const char *)a.k + (it.unit >= 0 ? it.row * a.cache_stride * 2 : 0)), 0,
+            it.unit >= 0 ? (int)(uint32_t)(a.n_ctx * kRowBytes) : 0, kBufferFlags);
+        SA_LDS char *tw = (SA_LDS char *)&t_lds[buf][0] + (NR * w) * kTStride;
 #pragma unroll
         for (int i = 0; i < NR; i++) {
-            const int slot = w * NR + i;
-            const int ij = __builtin_amdgcn_readlane(iv, key_of_slot(slot));
-            const char *rbase = ij >= 0 ? cbase + (int64_t)ij * kRowBytes : (const char *)g_zero_row;
-            dma16(rbase, (uint32_t)lane << 4, lds_addr(&t_lds[buf][slot * kTStride]));
+            const int ij = __builtin_amdgcn_readlane(iv, NR * w + i);
+            dma16_buf(rsrc, ((uint32_t)ij << 10) + ((uint32_t)lane << 4), lds_addr(tw + swap23(i) * kTStride));
         }
     };
 

@@ -62,6 +62,7 @@ __device__ __forceinline__ void lds_barrier() {
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
     return (uint32_t)(uintptr_t)(const SA_LDS void *)p;
 }
+__device__ __forceinline__ uint32_t lds_addr(const SA_LDS void *p) { return (uint32_t)(uintptr_t)p; }
 
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
@@ -72,6 +73,14 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
 __device__ __forceinline__ void dma16(const void *sbase, uint32_t voff, uint32_t lds) {
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 nt"
                  ::"s"(lds), "v"(voff), "s"(sbase) : "memory", "m0");
+}
+// The same gather through a buffer resource: lane i moves the 16 bytes at byte offset
+// voff_i of the resource to LDS address lds + 16 i. An offset past the resource's range
+// (a masked row's wrapped-around offset) reads as zeros, so masked rows need no
+// separate source and every lane's access stays inside the resource.
+__device__ __forceinline__ void dma16_buf(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds"
+                 ::"s"(lds), "v"(voff), "s"(rsrc) : "memory", "m0");
 }
 // Same with 4 bytes per lane (LDS address lds + 4 i).
 __device__ __forceinline__ void dma4(const void *sbase, uint32_t voff, uint32_t lds) {
@@ -107,7 +116,9 @@ __device__ __forceinline__ int swap23(int m) { return (m & ~12) | ((m & 4) << 1)
 constexpr int kKStride = kRowBytes + 16;
 
 // K slot s holds tile key (s & 32) | swap23(s & 31), so MFMA row m of key block kb
-// (which must hold key kb*32 + swap23(m)) reads slot kb*32 + m.
+// (which must hold key kb*32 + swap23(m)) reads slot kb*32 + m. The map is its own
+// inverse, and for keys n*w + i (n = 16 or 32, i < n) it is n*w + swap23(i): a wave that
+// gathers a run of n keys writes n slots at a wave base plus constant offsets.
 __device__ __forceinline__ int key_of_slot(int s) { return (s & 32) | swap23(s & 31); }
 
 // Map the linear workgroup id so that the workgroups of one query row (its head

@@ -59,6 +59,7 @@ def _decode(lib, **kw):
     (dict(rows=-1), L.SA_ERR_SHAPE),
     (dict(kmax=0), L.SA_ERR_SHAPE),
     (dict(n_ctx=0), L.SA_ERR_SHAPE),
+    (dict(n_ctx=4194304), L.SA_ERR_UNSUPPORTED),  # bf16 caches: at most 2^22 - 1 positions
     (dict(q=A16 + 8), L.SA_ERR_UNSUPPORTED),
     (dict(out=A16 + 4), L.SA_ERR_UNSUPPORTED),
     (dict(idx=A16 + 2), L.SA_ERR_UNSUPPORTED),

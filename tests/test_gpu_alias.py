@@ -150,3 +150,20 @@ def test_alias_sustained_sampled():
         assert_parity(out[r:r + 1].cpu().numpy(), ref, *BF16_TOL, f"alias sustained row {r}")
     del inp
     torch.cuda.empty_cache()
+
+
+def test_alias_masked_slots_read_zeros_after_nonfinite_tile():
+    """As for the separate path: row 0 (two tiles, both buffers) selects rows with +inf in
+    column 7; row 256, on the same workgroup next, has 5 keys, and its tile reuses a buffer
+    row 0 filled. The masked slots must read as zeros."""
+    c = aliased(w.decode_bf16(seed=97, batch=300, heads=64, n_ctx=256, k=128, name="alias masked after inf"))
+    c.k[0][c.idx[0, :128], 7] = 0x7F80
+    c.nsel[256] = 5
+    say("alias masked slots after an inf tile")
+    a, s = alias_and_separate(c)
+    assert torch.equal(a.view(torch.int32), s.view(torch.int32))
+    rows = [0, 1, 256, 257, 299]
+    ref = run_oracle(c, rows=rows)
+    got = a.cpu().numpy()
+    assert_parity(got[rows], ref[rows], *BF16_TOL, "alias masked after inf")
+    assert np.isfinite(got[256]).all()

@@ -298,3 +298,14 @@ def test_few_keys_precision():
     err = np.abs(got.astype(np.float64) - ref)
     say(f"  max abs error {err.max():.2e}")
     assert err.max() < 1e-4
+
+
+def test_masked_slots_read_zeros_after_nonfinite_tile():
+    """A workgroup's second unit (row 256 of 300) has 5 keys after its first unit (row 0)
+    filled the tile buffers with value rows holding +inf: the 59 masked slots must read
+    as zeros (a stale inf times the zero weight of a masked key would give NaN)."""
+    c = w.decode_bf16(seed=96, batch=300, heads=64, n_ctx=256, k=128, name="masked after inf")
+    c.v[0][c.idx[0, :128], 7] = 0x7F80  # +inf in column 7 of every row row 0 selects
+    c.nsel[256] = 5
+    got, ref = check_case(c, rows=[0, 1, 255, 256, 257, 299], label="masked slots after an inf tile")
+    assert np.isinf(got[0][:, 7]).all() and np.isfinite(got[256]).all()
