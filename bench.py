@@ -16,6 +16,18 @@ step), the step time, a roofline object for the dominant kernel (the attention
 decode kernel: algorithmic bytes per launch over its HIP-event-timed average
 duration, against 8 TB/s) and a cpu_baseline object (the float64 oracle timed
 on this host's cores on a bounded sample of the same workload).
+
+--workload selects other shapes of the same path (one JSON line each; the default
+is the decode step above):
+  decode-alias   the decode step with one latent tensor serving as K and V
+                 (each selected row gathered once)
+  prefill        2,048 query rows at positions 2,048..4,095 over one shared
+                 4,096-position cache: causal top-640 (valid_len = pos + 1), then
+                 prefill attention at 64 heads
+  prefill-h16    the same with 16 real heads, launched as 16 (the kernel pads to
+                 its 32-head block internally)
+  prefill-pad16  the same 16 heads copied into a zero-padded 32-head buffer with
+                 zero sinks, launched at 32 heads, real heads copied out
 """
 from __future__ import annotations
 
@@ -36,10 +48,11 @@ def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
 
-def algorithmic_bytes(rows: int, heads: int, d: int, k: int) -> int:
+def algorithmic_bytes(rows: int, heads: int, d: int, k: int, kv_tensors: int = 2) -> int:
     """Bytes the method itself moves per decode launch: bf16 q, the k gathered bf16 K and V
-    rows, the int32 index list and the fp32 output of every row, plus the fp32 sinks."""
-    per_row = 2 * heads * d + 2 * 2 * d * k + 4 * k + 4 * heads * d
+    rows (one gather when one tensor serves as both), the int32 index list and the fp32
+    output of every row, plus the fp32 sinks."""
+    per_row = 2 * heads * d + kv_tensors * 2 * d * k + 4 * k + 4 * heads * d
     return rows * per_row + 4 * heads
 
 
@@ -124,6 +137,8 @@ def main() -> int:
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--attn-only", action="store_true", help="time only the attention kernel (profiling)")
+    ap.add_argument("--workload", default="decode",
+                    choices=["decode", "decode-alias", "prefill", "prefill-h16", "prefill-pad16"])
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB, --steps times "
                          "(calibrates the HBM byte counters against a known size)")
@@ -155,12 +170,17 @@ def main() -> int:
                           "gbs_read_plus_write": 2 * n / dt / 1e9}), flush=True)
         return 0
     sa.load()
+    if args.workload.startswith("prefill"):
+        return bench_prefill(args, torch, sa, w, dev)
     B, H, N, K = args.batch, args.heads, args.n_ctx, args.k
+    alias = args.workload == "decode-alias"
 
     log(f"[bench] generating 2 input sets: {B} sequences x {N} positions x {w.D} bf16 K and V each")
     sets = []
     for i in range(2):
         inp = w.device_decode_inputs(torch, dev, B, H, N, K, seed=args.seed + i)
+        if alias:  # one latent tensor as K and V
+            inp["v"] = inp["k"]
         g = torch.Generator(device=dev)
         g.manual_seed(args.seed + 100 + i)
         scores = torch.randn((B, N), generator=g, device=dev, dtype=torch.float32)
@@ -197,7 +217,7 @@ def main() -> int:
     attn_ms = sum(a.elapsed_time(b) for a, b in events) / args.steps
     ms_per_step = wall * 1e3 / args.steps
 
-    nbytes = algorithmic_bytes(B, H, w.D, K)
+    nbytes = algorithmic_bytes(B, H, w.D, K, kv_tensors=1 if alias else 2)
     flops = algorithmic_flops(B, H, w.D, K)
     achieved_gbs = nbytes / (attn_ms * 1e-3) / 1e9
     log(f"[bench] step {ms_per_step:.3f} ms, attention kernel {attn_ms:.3f} ms: {achieved_gbs:.0f} GB/s "
@@ -222,6 +242,7 @@ def main() -> int:
             "workload": f"decode: {B} independent sequences per step, {H} heads, head width {w.D}, "
                         f"{N} cached positions per sequence, indexer top-{K} over {N} fp32 scores per row, "
                         f"then sparse attention with per-head sinks over the {K} selected rows"
+                        + (" of one latent tensor serving as K and V" if alias else "")
                         + (" (attention only)" if args.attn_only else ""),
             "batch_rows": B, "heads": H, "head_dim": w.D, "n_ctx": N, "k": K,
         },
@@ -231,8 +252,9 @@ def main() -> int:
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved_gbs / HBM_PEAK_GBS,
-            "traffic": measured_traffic(B, H, N, K),
-            "kernel": "attn_bf16_kernel<2,8> (sparse_attn_decode)",
+            "traffic": None if alias else measured_traffic(B, H, N, K),
+            "kernel": "attn_bf16_alias_kernel<2,8> (sparse_attn_decode, K = V)" if alias
+                      else "attn_bf16_kernel<2,8> (sparse_attn_decode)",
             "kernel_ms": attn_ms,
             "algorithmic_bytes_per_launch": nbytes,
             "mfma_tflops": flops / (attn_ms * 1e-3) / 1e12,
@@ -243,6 +265,154 @@ def main() -> int:
         log("[bench] timing the float64 oracle on the host")
         result["cpu_baseline"], result["parity_sampled"] = cpu_baseline(
             inp, scores, out, inp["idx"] if args.attn_only else idx, H, K, args.cpu_budget, max_rows=B)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def prefill_cpu_baseline(q, kc, vc, sinks, scores, valid_len, out_gpu, idx_gpu, k, budget_s: float, max_rows: int):
+    """The float64 oracle (causal top-k over the row's scores, then attention over the
+    shared cache) on the host on a bounded sample of prefill rows, compared with the GPU."""
+    import numpy as np
+
+    import torch
+
+    import oracle
+    import workloads as w
+    threads = len(os.sched_getaffinity(0))
+    lib = oracle.load()
+
+    def bits(t):
+        return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+    kh, vh = bits(kc)[None], bits(vc)[None]
+    s_h = sinks.cpu().numpy().astype(np.float32)
+    out_host = out_gpu.cpu().numpy()
+    idx_host = idx_gpu.cpu().numpy()
+    vl_host = valid_len.cpu().numpy()
+    rows_done, t_total, max_err, ok = 0, 0.0, 0.0, True
+    while rows_done < max_rows and t_total < budget_s:
+        r = rows_done
+        qh = bits(q[r:r + 1])
+        sr = scores[r:r + 1].cpu().numpy()
+        t0 = time.perf_counter()
+        idx, cnt = oracle.topk(sr, k, vl_host[r:r + 1], lib=lib)
+        o = oracle.attention("bf16", qh, kh, vh, idx, cnt, s_h, w.SCALE, True, threads=threads, lib=lib)
+        t_total += time.perf_counter() - t0
+        g = out_host[r:r + 1].astype(np.float64)
+        fin = np.isfinite(o)
+        ok &= bool(np.array_equal(idx[0], idx_host[r]))
+        ok &= bool(np.array_equal(np.isnan(g), np.isnan(o)) and np.array_equal(np.isinf(g), np.isinf(o)))
+        err = np.abs(g[fin] - o[fin])
+        ok &= bool(np.all(err <= 2e-3))
+        max_err = max(max_err, float(err.max()) if err.size else 0.0)
+        rows_done += 1
+    heads = q.shape[1]
+    base = {"value": rows_done * heads / t_total, "unit": "query-rows*heads/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"the first {rows_done} of the segment's {q.shape[0]} rows (causal top-k over the row's "
+                      f"scores, then {heads}-head attention over the shared cache), {t_total:.1f} s of float64 "
+                      f"oracle work on {threads} OpenMP threads"}
+    parity = {"rows": rows_done, "indices_bit_exact_and_attention_within_tol": ok, "max_abs_err": max_err}
+    return base, parity
+
+
+def bench_prefill(args, torch, sa, w, dev) -> int:
+    """Prefill segment: T rows at positions first..first+T-1 over one shared cache; a step is
+    the causal top-k (valid_len = pos + 1) then prefill attention (with explicit 16 -> 32
+    head padding and copy-out for prefill-pad16)."""
+    T, N, K, first = 2048, 4096, 640, 2048
+    h_real = 16 if args.workload in ("prefill-h16", "prefill-pad16") else args.heads
+    pad = args.workload == "prefill-pad16"
+    h_launch = 32 if pad else h_real
+    D = w.D
+    log(f"[bench] prefill: {T} rows, {h_real} real heads (launch {h_launch}), shared cache of {N} positions")
+    sets = []
+    for i in range(2):
+        g = torch.Generator(device=dev)
+        g.manual_seed(args.seed + 200 + i)
+        st = {
+            "q": torch.randn((T, h_real, D), generator=g, device=dev).to(torch.bfloat16),
+            "k": torch.randn((N, D), generator=g, device=dev).to(torch.bfloat16),
+            "v": torch.randn((N, D), generator=g, device=dev).to(torch.bfloat16),
+            "sinks": torch.randn((h_real,), generator=g, device=dev),
+            "scores": torch.randn((T, N), generator=g, device=dev),
+            "valid_len": torch.arange(first + 1, first + T + 1, dtype=torch.int32, device=dev),
+            "idx": torch.empty((T, K), dtype=torch.int32, device=dev),
+            "cnt": torch.empty((T,), dtype=torch.int32, device=dev),
+            "out": torch.empty((T, h_real, D), dtype=torch.float32, device=dev),
+        }
+        if pad:
+            st["q_pad"] = torch.empty((T, h_launch, D), dtype=torch.bfloat16, device=dev)
+            st["s_pad"] = torch.empty((h_launch,), dtype=torch.float32, device=dev)
+            st["out_pad"] = torch.empty((T, h_launch, D), dtype=torch.float32, device=dev)
+        sets.append(st)
+    torch.cuda.synchronize()
+
+    def step(i, ev=None):
+        st = sets[i % 2]
+        sa.topk(st["scores"], K, valid_len=st["valid_len"], idx_out=st["idx"], count_out=st["cnt"])
+        if pad:
+            sa.pad_heads(st["q"], st["sinks"], h_launch, q_pad=st["q_pad"], s_pad=st["s_pad"])
+            q, sinks, out = st["q_pad"], st["s_pad"], st["out_pad"]
+        else:
+            q, sinks, out = st["q"], st["sinks"], st["out"]
+        if ev is not None:
+            ev[0].record()
+        sa.prefill(q, st["k"], st["v"], st["idx"], sinks, w.SCALE, st["cnt"], out=out)
+        if ev is not None:
+            ev[1].record()
+        if pad:
+            sa.unpad_heads(st["out_pad"], h_real, out=st["out"])
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    attn_ms = sum(a.elapsed_time(b) for a, b in events) / args.steps
+    ms_per_step = wall * 1e3 / args.steps
+    flops = T * 4 * h_real * D * K                 # useful work: the real heads
+    gathered = T * 2 * 2 * D * K                   # K and V rows staged from L2/MALL into LDS
+    unique = T * (2 * h_launch * D + 4 * K + 4 * h_launch * D) + 2 * 2 * N * D + 4 * h_launch
+    tflops = flops / (attn_ms * 1e-3) / 1e12
+    log(f"[bench] step {ms_per_step:.3f} ms, prefill kernel {attn_ms:.3f} ms: {tflops:.0f} TFLOP/s of real-head "
+        f"bf16 work ({tflops / MFMA_BF16_PEAK_TFLOPS:.1%} of MFMA peak), gathered {gathered / (attn_ms * 1e-3) / 1e9:.0f} GB/s")
+    st = sets[(args.steps - 1) % 2]
+    result = {
+        "metric": f"prefill query-rows*heads/s ({h_real} heads, d=512, k=640)",
+        "value": T * h_real / (ms_per_step * 1e-3),
+        "unit": "query-rows*heads/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded, generated on the device)",
+        "config": {
+            "workload": f"prefill: {T} query rows at positions {first}..{first + T - 1} over one shared "
+                        f"{N}-position cache, causal indexer top-{K} (valid_len = pos + 1), then sparse "
+                        f"attention with per-head sinks at {h_real} real heads"
+                        + (" padded to 32 with zero sinks and copied out" if pad else
+                           (" (launched as 16; the kernel pads to its 32-head block)" if h_real == 16 else "")),
+            "rows": T, "heads": h_real, "launch_heads": h_launch, "head_dim": D, "n_ctx": N, "k": K,
+        },
+        "roofline": {
+            "bound": "mfma", "achieved": tflops, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": tflops / MFMA_BF16_PEAK_TFLOPS, "traffic": None,
+            "kernel": f"attn_bf16_kernel<{2 if h_launch > 32 else 1},8> (sparse_attn_prefill)",
+            "kernel_ms": attn_ms, "algorithmic_flops_per_launch": flops,
+            "gathered_bytes_per_launch": gathered, "gathered_gbs": gathered / (attn_ms * 1e-3) / 1e9,
+            "unique_hbm_bytes_per_launch": unique,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the float64 oracle on the host")
+        result["cpu_baseline"], result["parity_sampled"] = prefill_cpu_baseline(
+            st["q"], st["k"], st["v"], st["sinks"], st["scores"], st["valid_len"], st["out"], st["idx"], K,
+            args.cpu_budget, max_rows=T)
     print(json.dumps(result), flush=True)
     return 0
 

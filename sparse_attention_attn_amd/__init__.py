@@ -118,27 +118,34 @@ def topk(scores: torch.Tensor, k: int, valid_len: Optional[torch.Tensor] = None,
     return idx_out, count_out
 
 
-def pad_heads(q: torch.Tensor, sinks: torch.Tensor, h_pad: int) -> Tuple[torch.Tensor, torch.Tensor]:
+def pad_heads(q: torch.Tensor, sinks: torch.Tensor, h_pad: int, q_pad: Optional[torch.Tensor] = None,
+              s_pad: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """sparse_attn_pad_heads: q [R, h, 512] -> [R, h_pad, 512] with zero heads; sinks -> zero-padded."""
     lib = load()
     rows, h, D = q.shape
     _need(q.is_cuda and q.is_contiguous() and sinks.is_contiguous() and sinks.dtype == torch.float32,
           "q and sinks must be contiguous device tensors, sinks float32")
-    q_pad = torch.empty((rows, h_pad, D), dtype=q.dtype, device=q.device)
-    s_pad = torch.empty((h_pad,), dtype=torch.float32, device=q.device)
+    if q_pad is None:
+        q_pad = torch.empty((rows, h_pad, D), dtype=q.dtype, device=q.device)
+    if s_pad is None:
+        s_pad = torch.empty((h_pad,), dtype=torch.float32, device=q.device)
+    _need(q_pad.shape == (rows, h_pad, D) and q_pad.dtype == q.dtype and q_pad.is_contiguous()
+          and s_pad.shape == (h_pad,) and s_pad.dtype == torch.float32, "q_pad / s_pad")
     rc = lib.sparse_attn_pad_heads(_dtype_code(q), _ptr(q), rows, h, h_pad, D, _ptr(sinks), _ptr(q_pad),
                                    _ptr(s_pad), _stream(q))
     _lib.check(rc, "sparse_attn_pad_heads", lib)
     return q_pad, s_pad
 
 
-def unpad_heads(out_pad: torch.Tensor, h_real: int) -> torch.Tensor:
+def unpad_heads(out_pad: torch.Tensor, h_real: int, out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """sparse_attn_unpad_heads: heads 0..h_real-1 of out_pad [R, h_pad, 512] (float32)."""
     lib = load()
     rows, h_pad, D = out_pad.shape
     _need(out_pad.is_cuda and out_pad.is_contiguous() and out_pad.dtype == torch.float32,
           "out_pad must be a contiguous float32 device tensor")
-    out = torch.empty((rows, h_real, D), dtype=torch.float32, device=out_pad.device)
+    if out is None:
+        out = torch.empty((rows, h_real, D), dtype=torch.float32, device=out_pad.device)
+    _need(out.shape == (rows, h_real, D) and out.dtype == torch.float32 and out.is_contiguous(), "out")
     rc = lib.sparse_attn_unpad_heads(_ptr(out_pad), rows, h_pad, h_real, D, _ptr(out), _stream(out_pad))
     _lib.check(rc, "sparse_attn_unpad_heads", lib)
     return out

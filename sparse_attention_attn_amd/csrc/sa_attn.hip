@@ -149,27 +149,27 @@ attn_bf16_kernel(AttnArgs a, int n_hg, int64_t units) {
     // LDS slot; lane i moves bytes [16i, 16i + 16) of the row. Wave w gathers keys
     // NK*w + i. The buffer resource spans the row's cache; a masked key (-1) has a
     // wrapped-around offset past its end and arrives as zeros.
-    auto dma_k = [&](const Item &it, int iv) {
-        const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)kbase_of(it), 0, (int)(uint32_t)(a.n_ctx * kRowBytes), kBufferFlags);
-        SA_LDS char *kw = (SA_LDS char *)k_lds + (NK * w) * kKStride;
-#pragma unroll
-        for (int i = 0; i < NK; i++) {
-            const int ij = __builtin_amdgcn_readlane(iv, NK * w + i);
-            dma16_buf(rsrc, ((uint32_t)ij << 10) + ((uint32_t)lane << 4), lds_addr(kw + swap23(i) * kKStride));
-        }
+    // Row DMAs are issued one at a time, spread through the tile's compute, so that the
+    // CU's address unit (16 cycles per 1 KiB row) never queues a burst of them.
+    auto rsrc_k = [&](const Item &it) {
+        return __builtin_amdgcn_make_buffer_rsrc((void *)kbase_of(it), 0, (int)(uint32_t)(a.n_ctx * kRowBytes),
+                                                 kBufferFlags);
+    };
+    auto rsrc_v = [&](const Item &it) {
+        return __builtin_amdgcn_make_buffer_rsrc(
+            (void *)vbase_of(it), 0, (int)(uint32_t)(a.n_ctx * kRowBytes - (int64_t)it.cs * VROW), kBufferFlags);
+    };
+    auto dma_k_row = [&](__amdgpu_buffer_rsrc_t rsrc, int iv, int i) {
+        const int ij = __builtin_amdgcn_readlane(iv, NK * w + i);
+        dma16_buf(rsrc, ((uint32_t)ij << 10) + ((uint32_t)lane << 4),
+                  lds_addr((SA_LDS char *)k_lds + (NK * w + swap23(i)) * kKStride));
     };
     // V rows keep the tile's key order; only the unit's column slice is moved.
-    auto dma_v = [&](const Item &it, int iv) {
-        const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)vbase_of(it), 0, (int)(uint32_t)(a.n_ctx * kRowBytes - (int64_t)it.cs * VROW), kBufferFlags);
-#pragma unroll
-        for (int i = 0; i < NV; i++) {
-            const int j = w * NV + i;
-            const int ij = __builtin_amdgcn_readlane(iv, j);
-            if (VCHUNKS == 64 || lane < VCHUNKS)
-                dma16_buf(rsrc, ((uint32_t)ij << 10) + ((uint32_t)lane << 4), lds_addr(v_lds + j * VSTRIDE));
-        }
+    auto dma_v_row = [&](__amdgpu_buffer_rsrc_t rsrc, int iv, int i) {
+        const int j = w * NV + i;
+        const int ij = __builtin_amdgcn_readlane(iv, j);
+        if (VCHUNKS == 64 || lane < VCHUNKS)
+            dma16_buf(rsrc, ((uint32_t)ij << 10) + ((uint32_t)lane << 4), lds_addr(v_lds + j * VSTRIDE));
     };
 
     // Per-unit state. Query operand of S^T = K Q^T over this wave's half kb of the head
@@ -252,12 +252,11 @@ attn_bf16_kernel(AttnArgs a, int n_hg, int64_t units) {
         }
     };
 
-    // Issue order per wave: Q/sink(0), I(0); then K(j), I(j+1), V(j) for the first item
-    // j = 0; then in iteration j: K(j+1) after the scores, followed on a unit's last tile
-    // by the next unit's query and sink (kQLoads); after the values I(j+2) and V(j+1),
+    // Issue order per wave: Q/sink(0), I(0) | drain | K(0), I(1); then in tile j: V(j)
+    // spread through the scores; K(j+1) spread through the softmax, followed on a unit's
+    // last tile by the next unit's query and sink (kQLoads); after the values I(j+2),
     // followed on a unit's last tile by its kStores output stores. Each wait below counts
-    // exactly the operations issued after the one it needs, so a query waits behind the
-    // gathers issued before it and stores are waited on only a full tile later.
+    // exactly the operations issued after the one it needs.
     Item cur = make_item(base);
     Item nx = next_item(cur);
     Item nx2 = next_item(nx);
@@ -268,20 +267,21 @@ attn_bf16_kernel(AttnArgs a, int n_hg, int64_t units) {
     start_unit();
     __builtin_amdgcn_s_waitcnt(0);  // nothing the compiler tracks is pending in the loop
     bool starting = false;          // the next unit's query is in flight
-    bool stores_out = false;        // the previous tile ended a unit: its stores follow V(j)
+    bool stores_out = false;        // the previous tile ended a unit: its stores follow I(j+1)
+    int iv_cur = resolve(cur, 0, bad);  // rows of the current tile (its V goes out with the scores)
     {
-        const int iv0 = resolve(cur, 0, bad);
-        dma_k(cur, iv0);
+        const __amdgpu_buffer_rsrc_t rk = rsrc_k(cur);
+#pragma unroll
+        for (int i = 0; i < NK; i++) dma_k_row(rk, iv_cur, i);
         dma_idx(nx, cur, 1);
-        dma_v(cur, iv0);
     }
 
     for (int j = 0; cur.unit >= 0; j++) {
         const bool more = nx.unit >= 0;
         const bool last_of_unit = !more || nx.unit != cur.unit;
-        // K(j) has landed for this wave (I(j+1) and V(j) may be in flight), and so has a
-        // new unit's query and sink (issued after K(j), before I(j+1), V(j) and stores).
-        if (stores_out) wait_vmcnt<vm_clamp(NV + 1 + kStores)>(); else wait_vmcnt<NV + 1>();
+        // K(j) has landed for this wave, and so has a unit's query and sink when tile j
+        // starts one. After K(j) come [Q] I(j+1) [stores]; a query is followed by both.
+        if (starting) wait_vmcnt<vm_clamp(1 + kStores)>(); else wait_vmcnt<1>();
         if (starting) {
             start_unit();
             starting = false;
@@ -294,6 +294,9 @@ attn_bf16_kernel(AttnArgs a, int n_hg, int64_t units) {
         {
             // Software-pipelined: the operands of step kk+1 are read before the two
             // MFMAs of step kk issue, so LDS latency hides behind the matrix pipe.
+            // The tile's V rows go out here, NV / 16 per step, in the matrix pipe's shadow
+            // (every wave finished the previous tile's values before the barrier above).
+            const __amdgpu_buffer_rsrc_t rv = rsrc_v(cur);
             const SA_LDS char *krow = (const SA_LDS char *)k_lds + ln * kKStride + 512 * kb + 256 * g;
             bf16x8 k0 = *(const SA_LDS bf16x8 *)(krow);
             bf16x8 k1 = *(const SA_LDS bf16x8 *)(krow + 32 * kKStride);
@@ -306,6 +309,8 @@ attn_bf16_kernel(AttnArgs a, int n_hg, int64_t units) {
                 }
                 sacc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qreg[kk], sacc0, 0, 0, 0);
                 sacc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qreg[kk], sacc1, 0, 0, 0);
+#pragma unroll
+                for (int r = 0; r < NV / 16; r++) dma_v_row(rv, iv_cur, kk * (NV / 16) + r);
                 __builtin_amdgcn_sched_barrier(0);
                 k0 = n0;
                 k1 = n1;
@@ -315,35 +320,36 @@ attn_bf16_kernel(AttnArgs a, int n_hg, int64_t units) {
         {
             const f32x16 give = kb ? sacc0 : sacc1;
 #pragma unroll
-            for (int e = 0; e < 16; e++) xch_lds[w][e][lane] = give[e];
+            for (int c = 0; c < 4; c++)  // chunk c of every lane is contiguous: 16-byte writes
+                ((f32x4 *)&xch_lds[w][0][0])[64 * c + lane] =
+                    (f32x4){give[4 * c], give[4 * c + 1], give[4 * c + 2], give[4 * c + 3]};
         }
         lds_barrier();  // partials exchanged; every wave is also done reading k_lds
 
-        // Indices of item j+1 have landed; start gathering its K (and on a unit's last
-        // tile the next unit's query: the scores were the last use of qreg).
-        if (stores_out) wait_vmcnt<vm_clamp(NV + kStores)>(); else wait_vmcnt<NV>();
+        // Indices of item j+1 have landed (after them: [stores], V(j)).
+        if (stores_out) wait_vmcnt<vm_clamp(kStores + NV)>(); else wait_vmcnt<NV>();
         int iv_n = 0;
         const bool q_now = last_of_unit && more;
-        if (more) {
-            iv_n = resolve(nx, (j + 1) & 1, nx.unit == cur.unit ? bad : bad_next);
-            dma_k(nx, iv_n);
-            if (q_now) load_q_async(nx);
-        }
+        if (more) iv_n = resolve(nx, (j + 1) & 1, nx.unit == cur.unit ? bad : bad_next);
+        const __amdgpu_buffer_rsrc_t rk = rsrc_k(nx);
 
         // Full scores of key block kb: (half 0 + half 1) of the head width, the same
         // sum in both waves of the pair. Element e of this lane is key
         // kb*32 + 16*(e/8) + 8g + e%8 of the tile.
         const f32x16 own = kb ? sacc1 : sacc0;
+        f32x4 part[4];
+#pragma unroll
+        for (int c = 0; c < 4; c++) part[c] = ((const f32x4 *)&xch_lds[w ^ 1][0][0])[64 * c + lane];
         float s[16];
         float mloc = -INFINITY;
 #pragma unroll
         for (int e = 0; e < 16; e++) {
-            const float full = own[e] + xch_lds[w ^ 1][e][lane];
+            const float full = own[e] + part[e >> 2][e & 3];
             const int p = cur.tile * kTile + kb * 32 + 16 * (e >> 3) + 8 * g + (e & 7);
             s[e] = p < cur.n ? full * scale2 : -INFINITY;
             mloc = fmaxf(mloc, s[e]);
         }
-        mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+        mloc = max_xor32(mloc);
         if (g == 0) max_lds[w][ln] = mloc;
         lds_barrier();  // maxima exchanged; every wave is done reading the partials
 
@@ -375,16 +381,24 @@ attn_bf16_kernel(AttnArgs a, int n_hg, int64_t units) {
         for (int e = 0; e < 16; e++) {
             const float pf = exp2_hw(s[e] - ref);
             const uint32_t pbits = __float_as_uint(pf);
-            const uint32_t trunc = pbits >> 16;
+            const uint32_t trunc = pbits >> 16;  // a NaN stays a NaN after either step below
             const bool exact = (pbits & 0xffffu) == 0u && pf > 0.0f;
-            const uint32_t hb = pf != pf ? 0x7fc0u : (exact ? trunc - 1u : trunc);
+            const uint32_t hb = exact ? trunc - 1u : trunc;
             const float hif = __uint_as_float(hb << 16);
             const __bf16 hi = __builtin_bit_cast(__bf16, (uint16_t)hb);
             const __bf16 lo = (__bf16)(pf - hif);
             psum += hif + (float)lo;
             if (e < 8) { ph0[e] = hi; pl0[e] = lo; } else { ph1[e - 8] = hi; pl1[e - 8] = lo; }
+            // The next tile's K rows go out here, NK / 16 per element (every wave is past
+            // this tile's scores, so the K buffer is free).
+            if (more) {
+#pragma unroll
+                for (int r = 0; r < NK / 16; r++) dma_k_row(rk, iv_n, e * (NK / 16) + r);
+            }
         }
-        psum += __shfl_xor(psum, 32);
+        // On a unit's last tile: the next unit's query (the scores were qreg's last use).
+        if (q_now) load_q_async(nx);
+        psum = sum_xor32(psum);
         bf16x8 *p_out = (bf16x8 *)&xch_lds[w][0][0];
         p_out[lane] = ph0;
         p_out[64 + lane] = ph1;
@@ -392,11 +406,9 @@ attn_bf16_kernel(AttnArgs a, int n_hg, int64_t units) {
         p_out[192 + lane] = pl1;
         if (g == 0) sum_lds[w][ln] = psum;
 
-        // V(j) has landed (stores, K(j+1) and a query may be in flight).
+        // V(j) has landed (after it: K(j+1), [Q]).
         if (!more) {
             wait_vmcnt<0>();
-        } else if (stores_out) {
-            if (q_now) wait_vmcnt<vm_clamp(kStores + NK + kQLoads)>(); else wait_vmcnt<vm_clamp(kStores + NK)>();
         } else {
             if (q_now) wait_vmcnt<NK + kQLoads>(); else wait_vmcnt<NK>();
         }
@@ -461,7 +473,7 @@ attn_bf16_kernel(AttnArgs a, int n_hg, int64_t units) {
         lds_barrier();  // every wave is done with v_lds and the P operands
 
         dma_idx(nx2, cur, j & 1);  // slot j&1 held item j's list, consumed above
-        if (more) dma_v(nx, iv_n);
+        iv_cur = iv_n;
         stores_out = last_of_unit;
         starting = q_now;
         if (last_of_unit) {

@@ -141,17 +141,18 @@ attn_bf16_alias_kernel(AttnArgs a, int n_hg, int64_t units) {
     // One DMA instruction per cache row (1 KiB): wave w gathers keys NR*w + i into slots
     // NR*w + swap23(i) of buffer buf. The buffer resource spans the row's cache; a masked
     // key (-1) has a wrapped-around offset past its end and arrives as zeros, and so does
-    // every row when there is no item (the resource is then empty).
-    auto dma_tile = [&](const Item &it, int iv, int buf) {
-        const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+    // every row when there is no item (the resource is then empty). The rows of one tile
+    // are issued one or two at a time through the next tile's scores, so the CU's address
+    // unit (16 cycles per 1 KiB row) never queues a burst of them.
+    auto rsrc_tile = [&](const Item &it) {
+        return __builtin_amdgcn_make_buffer_rsrc(
             (void *)((const char *)a.k + (it.unit >= 0 ? it.row * a.cache_stride * 2 : 0)), 0,
             it.unit >= 0 ? (int)(uint32_t)(a.n_ctx * kRowBytes) : 0, kBufferFlags);
-        SA_LDS char *tw = (SA_LDS char *)&t_lds[buf][0] + (NR * w) * kTStride;
-#pragma unroll
-        for (int i = 0; i < NR; i++) {
-            const int ij = __builtin_amdgcn_readlane(iv, NR * w + i);
-            dma16_buf(rsrc, ((uint32_t)ij << 10) + ((uint32_t)lane << 4), lds_addr(tw + swap23(i) * kTStride));
-        }
+    };
+    auto dma_tile_row = [&](__amdgpu_buffer_rsrc_t rsrc, int iv, int buf, int i) {
+        const int ij = __builtin_amdgcn_readlane(iv, NR * w + i);
+        dma16_buf(rsrc, ((uint32_t)ij << 10) + ((uint32_t)lane << 4),
+                  lds_addr((SA_LDS char *)&t_lds[buf][0] + (NR * w + swap23(i)) * kTStride));
     };
 
     const float scale2 = a.scale * kLog2e;
@@ -212,10 +213,12 @@ attn_bf16_alias_kernel(AttnArgs a, int n_hg, int64_t units) {
         }
     };
 
-    // Issue order per wave (end(j) = after tile j's values; mid(j) = after its scores):
-    //   prologue: Q(0), I(0), I(1) | drain | T(0), I(2), T(1)
+    // Issue order per wave (S(j) = tile j's scores; mid(j) = after them; end(j) = after its
+    // values):
+    //   prologue: Q(0), I(0), I(1) | drain | T(0), I(2)
+    //   S(j):     T(j+1), spread through the score steps
     //   mid(j):   Q(next unit) when j is a unit's last tile
-    //   end(j):   wait I(j+2); I(j+3), T(j+2), then the unit's stores when j is its last
+    //   end(j):   wait I(j+2); I(j+3), then the unit's stores when j is its last
     // The top of tile j waits for T(j) (and for Q when j starts a unit).
     Item cur = make_item(base, 0);
     Item nx = next_item(cur);
@@ -227,31 +230,34 @@ attn_bf16_alias_kernel(AttnArgs a, int n_hg, int64_t units) {
     wait_vmcnt<0>();
     start_unit();
     __builtin_amdgcn_s_waitcnt(0);  // nothing the compiler tracks is pending in the loop
+    int iv_next;                    // rows of tile j+1, gathered during tile j's scores
     {
         const int iv0 = resolve(cur, 0);
-        const int iv1 = resolve(nx, 1);
-        dma_tile(cur, iv0, 0);
+        iv_next = resolve(nx, 1);
+        const __amdgpu_buffer_rsrc_t r0 = rsrc_tile(cur);
+#pragma unroll
+        for (int i = 0; i < NR; i++) dma_tile_row(r0, iv0, 0, i);
         dma_idx(nx2, cur, 0);
-        dma_tile(nx, iv1, 1);
     }
-    bool last1 = false;  // tile j-1 ended a unit (its stores follow T(j+1); Q(j) precedes I(j+2))
-    bool last2 = false;  // tile j-2 ended a unit (its stores follow T(j))
+    bool last1 = false;  // tile j-1 ended a unit (its stores follow I(j+2); Q(j-1) precedes I(j+2))
 
     for (int j = 0; cur.unit >= 0; j++) {
         const bool more = nx.unit >= 0;
         const bool last_of_unit = !more || nx.unit != cur.unit;
         const int buf = j & 1;
         // T(j) has landed, and the query of a unit that starts here. Issued after T(j):
-        // [stores(j-2)] [Q(j-1)] I(j+2) T(j+1) [stores(j-1)]; when tile j starts a unit,
-        // the wait is for Q(j-1), after which come I(j+2), T(j+1) and stores(j-1).
-        if (last1) wait_vmcnt_dyn(1 + NR + kStores);
-        else wait_vmcnt_dyn((last2 ? kStores : 0) + 1 + NR);
+        // [Q(j-1)] I(j+2) [stores(j-1)]; when tile j starts a unit, the wait is for Q(j-1),
+        // after which come I(j+2) and the stores.
+        if (last1) wait_vmcnt<vm_clamp(1 + kStores)>(); else wait_vmcnt<1>();
         if (last1) start_unit();
         lds_barrier();
 
         // ---- partial scores over this wave's half of the head width (tile as K).
         f32x16 sacc0 = (f32x16){}, sacc1 = (f32x16){};
         {
+            // T(j+1) goes out here into the other buffer (every wave finished tile j-1's
+            // values, which used it, before the barrier above).
+            const __amdgpu_buffer_rsrc_t rt = rsrc_tile(nx);
             const SA_LDS char *krow = (const SA_LDS char *)&t_lds[buf][0] + ln * kTStride + 512 * kb + 256 * g;
             bf16x8 k0 = *(const SA_LDS bf16x8 *)(krow);
             bf16x8 k1 = *(const SA_LDS bf16x8 *)(krow + 32 * kTStride);
@@ -264,6 +270,8 @@ attn_bf16_alias_kernel(AttnArgs a, int n_hg, int64_t units) {
                 }
                 sacc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qreg[kk], sacc0, 0, 0, 0);
                 sacc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qreg[kk], sacc1, 0, 0, 0);
+#pragma unroll
+                for (int r = 0; r < NR / 16; r++) dma_tile_row(rt, iv_next, buf ^ 1, kk * (NR / 16) + r);
                 __builtin_amdgcn_sched_barrier(0);
                 k0 = n0;
                 k1 = n1;
@@ -272,7 +280,9 @@ attn_bf16_alias_kernel(AttnArgs a, int n_hg, int64_t units) {
         {
             const f32x16 give = kb ? sacc0 : sacc1;
 #pragma unroll
-            for (int e = 0; e < 16; e++) xch_lds[w][e][lane] = give[e];
+            for (int c = 0; c < 4; c++)  // chunk c of every lane is contiguous: 16-byte writes
+                ((f32x4 *)&xch_lds[w][0][0])[64 * c + lane] =
+                    (f32x4){give[4 * c], give[4 * c + 1], give[4 * c + 2], give[4 * c + 3]};
         }
         lds_barrier();
 
@@ -281,16 +291,19 @@ attn_bf16_alias_kernel(AttnArgs a, int n_hg, int64_t units) {
         if (q_now) load_q_async(nx);
 
         const f32x16 own = kb ? sacc1 : sacc0;
+        f32x4 part[4];
+#pragma unroll
+        for (int c = 0; c < 4; c++) part[c] = ((const f32x4 *)&xch_lds[w ^ 1][0][0])[64 * c + lane];
         float s[16];
         float mloc = -INFINITY;
 #pragma unroll
         for (int e = 0; e < 16; e++) {
-            const float full = own[e] + xch_lds[w ^ 1][e][lane];
+            const float full = own[e] + part[e >> 2][e & 3];
             const int p = cur.tile * kTile + kb * 32 + 16 * (e >> 3) + 8 * g + (e & 7);
             s[e] = p < cur.n ? full * scale2 : -INFINITY;
             mloc = fmaxf(mloc, s[e]);
         }
-        mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+        mloc = max_xor32(mloc);
         if (g == 0) max_lds[w][ln] = mloc;
         lds_barrier();
 
@@ -326,7 +339,7 @@ attn_bf16_alias_kernel(AttnArgs a, int n_hg, int64_t units) {
             psum += hif + (float)lo;
             if (e < 8) { ph0[e] = hi; pl0[e] = lo; } else { ph1[e - 8] = hi; pl1[e - 8] = lo; }
         }
-        psum += __shfl_xor(psum, 32);
+        psum = sum_xor32(psum);
         bf16x8 *p_out = (bf16x8 *)&xch_lds[w][0][0];
         p_out[lane] = ph0;
         p_out[64 + lane] = ph1;
@@ -388,11 +401,10 @@ attn_bf16_alias_kernel(AttnArgs a, int n_hg, int64_t units) {
         }
         lds_barrier();  // every wave is done with this tile buffer and the P operands
 
-        // I(j+2) has landed: after it come T(j+1), [stores(j-1)], [Q(j)].
-        wait_vmcnt_dyn(NR + (last1 ? kStores : 0) + (q_now ? kQLoads : 0));
-        const int iv2 = resolve(nx2, buf);
+        // I(j+2) has landed: after it come [stores(j-1)], T(j+1), [Q(j)].
+        wait_vmcnt_dyn((last1 ? kStores : 0) + NR + (q_now ? kQLoads : 0));
+        iv_next = resolve(nx2, buf);
         dma_idx(nx3, cur, buf ^ 1);  // slot buf^1 held I(j+1), resolved at end(j-1)
-        dma_tile(nx2, iv2, buf);
         if (last_of_unit) {
             leave_unit(cur, bad0);
             bad0 = bad1;
@@ -400,7 +412,6 @@ attn_bf16_alias_kernel(AttnArgs a, int n_hg, int64_t units) {
             bad2 = false;
             cur_useq++;
         }
-        last2 = last1;
         last1 = last_of_unit;
         cur = nx;
         nx = nx2;

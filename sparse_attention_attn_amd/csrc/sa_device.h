@@ -103,6 +103,18 @@ __device__ __forceinline__ void register_ready(T &v) {
     asm volatile("" : "+v"(v));
 }
 
+// max(x[l], x[l ^ 32]) and x[l & 31] + x[l | 32] in every lane l: one v_permlane32_swap
+// hands each half of the wave the other half's values (no LDS round trip), and both
+// halves add in the same order, so the pair of lanes holds identical results.
+__device__ __forceinline__ float max_xor32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Bits 2 and 3 of m exchanged. Row m of a 32-key MFMA block holds key pi(m), which
 // makes each lane's sixteen scores two runs of eight consecutive keys (the P operand).
 __device__ __forceinline__ int swap23(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
