@@ -253,8 +253,8 @@ attn_bf16_kernel(AttnArgs a, int n_hg, int64_t units) {
     };
 
     // Issue order per wave: Q/sink(0), I(0) | drain | K(0), I(1); then in tile j: V(j)
-    // spread through the scores; K(j+1) spread through the softmax, followed on a unit's
-    // last tile by the next unit's query and sink (kQLoads); after the values I(j+2),
+    // spread through the scores; on a unit's last tile the next unit's query and sink
+    // (kQLoads) once V(j) has landed; K(j+1) spread through the values; then I(j+2),
     // followed on a unit's last tile by its kStores output stores. Each wait below counts
     // exactly the operations issued after the one it needs.
     Item cur = make_item(base);
@@ -279,8 +279,9 @@ attn_bf16_kernel(AttnArgs a, int n_hg, int64_t units) {
     for (int j = 0; cur.unit >= 0; j++) {
         const bool more = nx.unit >= 0;
         const bool last_of_unit = !more || nx.unit != cur.unit;
-        // K(j) has landed for this wave, and so has a unit's query and sink when tile j
-        // starts one. After K(j) come [Q] I(j+1) [stores]; a query is followed by both.
+        // K(j) has landed for this wave, and with it a unit's query and sink when tile j
+        // starts one (issued just before K(j)). After K(j) come I(j+1) and, when tile j
+        // starts a unit, the previous unit's stores.
         if (starting) wait_vmcnt<vm_clamp(1 + kStores)>(); else wait_vmcnt<1>();
         if (starting) {
             start_unit();
@@ -389,15 +390,7 @@ attn_bf16_kernel(AttnArgs a, int n_hg, int64_t units) {
             const __bf16 lo = (__bf16)(pf - hif);
             psum += hif + (float)lo;
             if (e < 8) { ph0[e] = hi; pl0[e] = lo; } else { ph1[e - 8] = hi; pl1[e - 8] = lo; }
-            // The next tile's K rows go out here, NK / 16 per element (every wave is past
-            // this tile's scores, so the K buffer is free).
-            if (more) {
-#pragma unroll
-                for (int r = 0; r < NK / 16; r++) dma_k_row(rk, iv_n, e * (NK / 16) + r);
-            }
         }
-        // On a unit's last tile: the next unit's query (the scores were qreg's last use).
-        if (q_now) load_q_async(nx);
         psum = sum_xor32(psum);
         bf16x8 *p_out = (bf16x8 *)&xch_lds[w][0][0];
         p_out[lane] = ph0;
@@ -406,12 +399,11 @@ attn_bf16_kernel(AttnArgs a, int n_hg, int64_t units) {
         p_out[192 + lane] = pl1;
         if (g == 0) sum_lds[w][ln] = psum;
 
-        // V(j) has landed (after it: K(j+1), [Q]).
-        if (!more) {
-            wait_vmcnt<0>();
-        } else {
-            if (q_now) wait_vmcnt<NK + kQLoads>(); else wait_vmcnt<NK>();
-        }
+        // V(j) has landed: nothing was issued after it.
+        wait_vmcnt<0>();
+        // On a unit's last tile: the next unit's query (the scores were qreg's last use),
+        // ahead of the K rows, so the wait for K(j+1) covers it too.
+        if (q_now) load_q_async(nx);
         lds_barrier();
 
         l_run = alpha * l_run + (sum_lds[2 * hb][ln] + sum_lds[2 * hb + 1][ln]);
@@ -465,6 +457,12 @@ attn_bf16_kernel(AttnArgs a, int n_hg, int64_t units) {
             for (int ks = 0; ks < 4; ks++) {
                 acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vcur[ks], pop[ks], acc[nt], 0, 0, 0);
                 acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vcur[ks], pol[ks], acc[nt], 0, 0, 0);
+            }
+            // The next tile's K rows go out here, NK / NT per column group, in the matrix
+            // pipe's shadow (every wave is past this tile's scores: the K buffer is free).
+            if (more) {
+#pragma unroll
+                for (int r = 0; r < NK / NT; r++) dma_k_row(rk, iv_n, nt * (NK / NT) + r);
             }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll

@@ -252,12 +252,13 @@ attn_bf16_alias_kernel(AttnArgs a, int n_hg, int64_t units) {
         if (last1) start_unit();
         lds_barrier();
 
+        const __amdgpu_buffer_rsrc_t rt = rsrc_tile(nx);  // T(j+1)
         // ---- partial scores over this wave's half of the head width (tile as K).
         f32x16 sacc0 = (f32x16){}, sacc1 = (f32x16){};
         {
-            // T(j+1) goes out here into the other buffer (every wave finished tile j-1's
-            // values, which used it, before the barrier above).
-            const __amdgpu_buffer_rsrc_t rt = rsrc_tile(nx);
+            // The first half of T(j+1) goes out here into the other buffer (every wave
+            // finished tile j-1's values, which used it, before the barrier above); the
+            // second half goes out during this tile's values.
             const SA_LDS char *krow = (const SA_LDS char *)&t_lds[buf][0] + ln * kTStride + 512 * kb + 256 * g;
             bf16x8 k0 = *(const SA_LDS bf16x8 *)(krow);
             bf16x8 k1 = *(const SA_LDS bf16x8 *)(krow + 32 * kTStride);
@@ -271,7 +272,8 @@ attn_bf16_alias_kernel(AttnArgs a, int n_hg, int64_t units) {
                 sacc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qreg[kk], sacc0, 0, 0, 0);
                 sacc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qreg[kk], sacc1, 0, 0, 0);
 #pragma unroll
-                for (int r = 0; r < NR / 16; r++) dma_tile_row(rt, iv_next, buf ^ 1, kk * (NR / 16) + r);
+                for (int r = kk * (NR / 2) / 16; r < (kk + 1) * (NR / 2) / 16; r++)
+                    dma_tile_row(rt, iv_next, buf ^ 1, r);
                 __builtin_amdgcn_sched_barrier(0);
                 k0 = n0;
                 k1 = n1;
@@ -395,6 +397,14 @@ attn_bf16_alias_kernel(AttnArgs a, int n_hg, int64_t units) {
                 else if (ks + 1 < 4) vn = read_v(ks + 1, 0);
                 acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vc, ph, acc[nt], 0, 0, 0);
                 acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vc, pl, acc[nt], 0, 0, 0);
+                // Second half of T(j+1), spread over the 4 NT key-step x column-group pairs.
+                {
+                    constexpr int kSteps = 4 * NT;
+                    const int st = ks * NT + nt;
+#pragma unroll
+                    for (int r = st * (NR / 2) / kSteps; r < (st + 1) * (NR / 2) / kSteps; r++)
+                        dma_tile_row(rt, iv_next, buf ^ 1, NR / 2 + r);
+                }
                 __builtin_amdgcn_sched_barrier(0);
                 vc = vn;
             }
