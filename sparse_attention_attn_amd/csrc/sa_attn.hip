@@ -367,7 +367,10 @@ attn_bf16_kernel(AttnArgs a, int n_hg, int64_t units) {
         float alpha = 1.0f;
         if (rescale) {
             const float ref_new = (m_new == -INFINITY) ? 0.0f : m_new;
-            alpha = exp2_hw(ref - ref_new);
+            // Nothing accumulated yet (l = 0, from a -inf sink): the old reference may be
+            // arbitrarily far above the new one, and 0 (not 2^(r - r'), which can overflow
+            // to inf and make inf * 0) keeps l and acc at 0.
+            alpha = l_run == 0.0f ? 0.0f : exp2_hw(ref - ref_new);
             ref = ref_new;
         }
         // p = hi + lo with both parts bf16, so the value product (one MFMA per part) sees
@@ -514,6 +517,11 @@ AttnPlan plan_attn_bf16(int64_t rows, int H) {
     else if (rows_hg < 256) nt = 4;
     p.cols_per_wg = 64 * nt;
     p.units = rows_hg * (kHeadDim / p.cols_per_wg);
+    if (hb == 2) {  // the eight-wave kernel
+        p.threads = 512;
+        p.lds_bytes = attn_bf16_ks_lds_bytes(p.cols_per_wg, false);
+        return p;
+    }
     p.threads = 128 * hb;
     p.lds_bytes = lds_bytes_of(hb, nt);
     return p;
@@ -539,14 +547,7 @@ hipError_t launch_attn_bf16(const AttnArgs &a, hipStream_t s) {
     if (p.units == 0) return hipSuccess;
     const int64_t grid = p.units < cu_count() ? p.units : cu_count();
     const int nt = p.cols_per_wg / 64;
-    if (p.heads_per_wg == 64) {
-        switch (nt) {
-            case 1: return launch_variant<2, 1>(a, p.units, grid, s);
-            case 2: return launch_variant<2, 2>(a, p.units, grid, s);
-            case 4: return launch_variant<2, 4>(a, p.units, grid, s);
-            default: return launch_variant<2, 8>(a, p.units, grid, s);
-        }
-    }
+    if (p.heads_per_wg == 64) return launch_attn_bf16_ks(a, p.cols_per_wg, p.units, s);
     switch (nt) {
         case 1: return launch_variant<1, 1>(a, p.units, grid, s);
         case 2: return launch_variant<1, 2>(a, p.units, grid, s);

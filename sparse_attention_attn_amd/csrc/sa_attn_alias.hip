@@ -38,24 +38,6 @@ namespace {
 
 constexpr int kTStride = kRowBytes + 80;  // 1104: 80 (mod 256)
 
-// s_waitcnt vmcnt(n) for a wave-uniform n formed at run time (clamped to 0..63; a
-// smaller count only waits longer).
-__device__ __forceinline__ void wait_vmcnt_dyn(int n) {
-    n = n < 0 ? 0 : (n > 63 ? 63 : n);
-    switch (__builtin_amdgcn_readfirstlane(n)) {
-#define SA_W(N) case N: wait_vmcnt<N>(); break;
-        SA_W(0) SA_W(1) SA_W(2) SA_W(3) SA_W(4) SA_W(5) SA_W(6) SA_W(7) SA_W(8) SA_W(9)
-        SA_W(10) SA_W(11) SA_W(12) SA_W(13) SA_W(14) SA_W(15) SA_W(16) SA_W(17) SA_W(18) SA_W(19)
-        SA_W(20) SA_W(21) SA_W(22) SA_W(23) SA_W(24) SA_W(25) SA_W(26) SA_W(27) SA_W(28) SA_W(29)
-        SA_W(30) SA_W(31) SA_W(32) SA_W(33) SA_W(34) SA_W(35) SA_W(36) SA_W(37) SA_W(38) SA_W(39)
-        SA_W(40) SA_W(41) SA_W(42) SA_W(43) SA_W(44) SA_W(45) SA_W(46) SA_W(47) SA_W(48) SA_W(49)
-        SA_W(50) SA_W(51) SA_W(52) SA_W(53) SA_W(54) SA_W(55) SA_W(56) SA_W(57) SA_W(58) SA_W(59)
-        SA_W(60) SA_W(61) SA_W(62)
-#undef SA_W
-        default: wait_vmcnt<63>(); break;
-    }
-}
-
 // Kernel template: HB head blocks of 32 (2*HB waves), NT 32-column output groups per
 // wave. Wave w: head block hb = w/2, kb = w%2 (half of the head width for the scores,
 // key block it finishes, half of the columns it accumulates), as in sa_attn.hip.
@@ -317,7 +299,10 @@ attn_bf16_alias_kernel(AttnArgs a, int n_hg, int64_t units) {
         float alpha = 1.0f;
         if (rescale) {
             const float ref_new = (m_new == -INFINITY) ? 0.0f : m_new;
-            alpha = exp2_hw(ref - ref_new);
+            // Nothing accumulated yet (l = 0, from a -inf sink): the old reference may be
+            // arbitrarily far above the new one, and 0 (not 2^(r - r'), which can overflow
+            // to inf and make inf * 0) keeps l and acc at 0.
+            alpha = l_run == 0.0f ? 0.0f : exp2_hw(ref - ref_new);
             ref = ref_new;
         }
         // p = hi + lo with both parts bf16, so the value product (one MFMA per part) sees
@@ -447,14 +432,7 @@ hipError_t launch_attn_bf16_alias(const AttnArgs &a, hipStream_t s) {
     const int64_t cus = device_cu_count();
     const int64_t grid = p.units < cus ? p.units : cus;
     const int nt = p.cols_per_wg / 64;
-    if (p.heads_per_wg == 64) {
-        switch (nt) {
-            case 1: return launch_variant<2, 1>(a, p.units, grid, s);
-            case 2: return launch_variant<2, 2>(a, p.units, grid, s);
-            case 4: return launch_variant<2, 4>(a, p.units, grid, s);
-            default: return launch_variant<2, 8>(a, p.units, grid, s);
-        }
-    }
+    if (p.heads_per_wg == 64) return launch_attn_bf16_ks(a, p.cols_per_wg, p.units, s);
     switch (nt) {
         case 1: return launch_variant<1, 1>(a, p.units, grid, s);
         case 2: return launch_variant<1, 2>(a, p.units, grid, s);

@@ -1,0 +1,738 @@
+// sa_attn_ks.hip -- gathered sparse attention with per-head sinks, bf16 storage, for
+// gfx950: the kernels for blocks of 64 heads, with every tile's keys split between two
+// halves of an eight-wave workgroup. One kernel reads separate K and V caches, the other
+// one cache serving as both (each selected row is then gathered once).
+//
+// What it computes (the same operation as sa_attn.hip): akol1/TensorFold pull request 4
+// ("DeepSeek V4.1: sparse attention on eight SIMD groups, the same bytes"), first commit
+// message: for a query row and its heads, the selected keys are scored in 64-key tiles
+// against a 512-wide head, with a running maximum, a tile sum and a value sum. TensorFold
+// pull request 1206, "What changes": every head has a sink logit (zero for padded heads).
+//
+// How it maps to CDNA4:
+//   * One workgroup serves one query row, 64 heads and 512/NS output columns, on eight
+//     waves, two per SIMD. Wave w takes heads 16(w&3) .. +15 of the block and key half
+//     kh = w>>2 of every 64-key tile: keys 32kh .. 32kh+31. Each wave keeps its own
+//     online softmax over its key half; at the end of a unit the two waves that hold the
+//     same heads combine their states through LDS, in a fixed order (half 0, half 1).
+//   * S^T = K Q^T and O^T = V^T P^T run on v_mfma_f32_16x16x32_bf16 with the 16 heads on
+//     the N side. The query (16 heads x 512) stays in 64 registers, so every score is
+//     contracted over the full head width inside one wave.
+//   * K rows sit in the order that makes each lane's four scores of a 16-slot block, for
+//     blocks 0 and 1, exactly the eight weights of its P^T operand (keys 8g .. 8g+7 of
+//     lane group g). So no score, maximum, sum or weight crosses a wave inside a tile: the
+//     row maximum and the tile sum are in-lane reductions plus two lane swaps
+//     (v_permlane16_swap, v_permlane32_swap). The barriers left are those that hand a
+//     gathered buffer from the waves that filled it to the waves that read it, and back.
+//   * Gathers are index-driven direct-to-LDS DMAs through buffer resources (a masked key
+//     reads zeros), issued one row at a time inside the MFMA loops.
+//   * Splitting work across workgroups only ever splits heads and output columns, never
+//     keys, so results are bit-identical across launch shapes and repeats, and the two
+//     kernels give the same bits on equal contents.
+//
+// Numerics, in log2 units (x2 = x * log2 e), per wave and 32-key half tile: m' = max(m,
+// max_j s_j); the exponent reference r moves to m' (0 if m' = -inf) with alpha = 2^(r - r')
+// (0 while nothing has been accumulated) when m' > r + 8 or r > m' > -inf for one of the
+// wave's 16 heads, else alpha = 1; p_j = 2^(s_j - r) split into hi + lo, both bf16; l =
+// alpha*l + sum_j (hi + lo); acc = alpha*acc + (hi + lo) V. Half 0 starts from the sink
+// (m = sink, r = sink or 0 if -inf, l = 2^(sink - r)), half 1 from nothing (m = -inf, r = 0,
+// l = 0). End: with R the reference of the half holding the larger maximum and a_h =
+// 2^(r_h - R) (0 for a half with l = 0), out = (a_0 acc_0 + a_1 acc_1) / (a_0 l_0 + a_1 l_1).
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "sa_device.h"
+#include "sa_internal.h"
+
+namespace sa {
+namespace {
+
+constexpr int kWaves = 8;
+constexpr int kRows = kTile / kWaves;   // rows each wave gathers per tile (per buffer)
+
+// K slot, within a 32-key half, of key kap = 8g + 4b + r: slot 16b + 4g + r. Row 4g + r of
+// the score MFMA over slots 16b .. 16b+15 lands in lane group g, element r, which is the
+// P^T operand's element 4b + r (key 8g + 4b + r).
+__device__ __forceinline__ int kslot_of_key(int kap) { return ((kap & 4) << 2) | ((kap >> 3) << 2) | (kap & 3); }
+
+// LDS row stride of the separate kernel's V buffer: the row bytes plus 32, an odd multiple
+// of 32 for every slice width. A transposing read of the value MFMA's operand touches
+// eight consecutive V slots (V slot of key kap: swap23(kap)) at one 32-byte column
+// window; with an odd multiple of 32 as stride they land on eight different bank windows.
+constexpr int vstride_of(int vrow) { return vrow + 32; }
+
+// Chunk swizzle of the aliased kernel's tile rows (stride 1024): the 16-byte chunk c of
+// the row in slot s is stored at chunk c ^ tswz(s). The score reads (sixteen slots
+// 16b .. 16b+15, one chunk) see sixteen different values of tswz and so sixteen bank
+// groups; the value reads (slots 16t2 + 0..7, or + 8..15, one aligned 32-byte window) see
+// eight different even (or odd) values, which keep each window whole and move the eight
+// windows to eight different places.
+__device__ __forceinline__ int tswz(int s) { return ((s & 7) << 1) | ((s >> 3) & 1); }
+
+template <typename T>
+__device__ __forceinline__ const SA_LDS T *lds_at(uint32_t addr) {
+    return (const SA_LDS T *)(uintptr_t)addr;
+}
+
+// Online-softmax state of one wave over its key half, relative to the reference ref.
+struct HalfState {
+    float m, ref, l;
+};
+
+template <int CB>
+__device__ __forceinline__ void half_start(HalfState &st, f32x4 (&acc)[CB], bool with_sink, float sink) {
+    if (with_sink) {
+        const float sink2 = sink * kLog2e;
+        st.m = sink2;
+        st.ref = (sink2 == -INFINITY) ? 0.0f : sink2;
+        st.l = exp2_hw(sink2 - st.ref);
+    } else {
+        st.m = -INFINITY;
+        st.ref = 0.0f;
+        st.l = 0.0f;
+    }
+#pragma unroll
+    for (int cb = 0; cb < CB; cb++) acc[cb] = (f32x4){};
+}
+
+// One half tile. s0, s1: the score MFMA blocks; element 4b + r of this lane is key p0 + 4b
+// + r of the row's list (p0 = 64 tile + 32 kh + 8 g); keys at or past n are masked. Returns
+// the two bf16 parts of the weights as the P^T operand, and updates the state and acc.
+template <int CB>
+__device__ __forceinline__ void half_tile(const f32x4 &s0, const f32x4 &s1, int p0, int n, float scale2,
+                                          HalfState &st, f32x4 (&acc)[CB], bf16x8 &ph, bf16x8 &pl) {
+    float s[8];
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 8; e++) {
+        const float full = e < 4 ? s0[e] : s1[e - 4];
+        s[e] = p0 + e < n ? full * scale2 : -INFINITY;
+        mloc = fmaxf(mloc, s[e]);
+    }
+    mloc = max_xor32(max_xor16(mloc));
+    const float m_new = fmaxf(st.m, mloc);
+    // The reference follows the running maximum lazily: it moves (and l, acc are rescaled
+    // by alpha) only when the maximum has risen more than kLazy above it, or when it sits
+    // above a finite maximum (from the start value 0); the decision is taken for the
+    // wave's 16 heads together. Otherwise alpha = 1 and every p stays <= 2^kLazy.
+    const bool move = m_new > st.ref + kLazy || (m_new < st.ref && m_new != -INFINITY);
+    const bool rescale = __builtin_amdgcn_ballot_w64(move) != 0;
+    float alpha = 1.0f;
+    if (rescale) {
+        const float ref_new = (m_new == -INFINITY) ? 0.0f : m_new;
+        // Nothing accumulated yet (l = 0): the old reference may be arbitrarily far from
+        // the new one, and 0 (not 2^(r - r'), which can overflow) keeps acc at 0.
+        alpha = st.l == 0.0f ? 0.0f : exp2_hw(st.ref - ref_new);
+        st.ref = ref_new;
+    }
+    // p = hi + lo with both parts bf16, so the value product (one MFMA per part) sees p
+    // to about 16 significant bits and l sums the same hi + lo. hi is p truncated toward
+    // zero and lo = bf16(p - hi); when p is itself a positive bf16 value, hi is the next
+    // bf16 below it and lo its last unit, so hi + lo = p exactly, and an infinite value
+    // times a positive weight stays infinite.
+    float psum = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; e++) {
+        const float pf = exp2_hw(s[e] - st.ref);
+        const uint32_t pbits = __float_as_uint(pf);
+        const uint32_t trunc = pbits >> 16;  // a NaN stays a NaN after either step below
+        const bool exact = (pbits & 0xffffu) == 0u && pf > 0.0f;
+        const uint32_t hb = exact ? trunc - 1u : trunc;
+        const float hif = __uint_as_float(hb << 16);
+        const __bf16 hi = __builtin_bit_cast(__bf16, (uint16_t)hb);
+        const __bf16 lo = (__bf16)(pf - hif);
+        psum += hif + (float)lo;
+        ph[e] = hi;
+        pl[e] = lo;
+    }
+    psum = sum_xor32(sum_xor16(psum));
+    st.l = __builtin_fmaf(alpha, st.l, psum);
+    st.m = m_new;
+    if (rescale) [[unlikely]] {
+#pragma unroll
+        for (int cb = 0; cb < CB; cb++) acc[cb] *= alpha;
+    }
+}
+
+// End of a unit: combine the two key halves and store. The pair (w, w ^ 4) holds the same
+// heads; wave kh finalises column blocks OWN*kh .. OWN*kh + OWN-1 in two rounds of OWN/2.
+// Per round each wave writes the partner's blocks (16-byte pieces, lane-major) into its
+// slot of xch (a free gathered buffer) and reads its own from the partner's slot. Lane
+// (g, l16) holds head l16, columns 16cb + 4g + 0..3: one 16-byte store per block. The
+// stores go through a buffer resource spanning the output row; a head past H stores past
+// its end, which the hardware drops, so every wave issues exactly OWN stores.
+template <int KH, int CB>
+__device__ __forceinline__ void combine_store(const HalfState &st, const f32x4 (&acc)[CB], float (*meta)[3][16],
+                                              f32x4 *xch, int w, int lane, int g, int l16, float *orow, int H,
+                                              int head, int col0, bool bad) {
+    constexpr int OWN = CB / 2;
+    constexpr int HALF = OWN / 2;
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(orow, 0, H * kHeadDim * 4, kBufferFlags);
+    if (g == 0) {
+        meta[w][0][l16] = st.m;
+        meta[w][1][l16] = st.ref;
+        meta[w][2][l16] = st.l;
+    }
+    // x * 1 is x exactly and x * NaN is NaN: a select of constants, so the divide is not
+    // put behind a branch and the store count stays the same on every path.
+    const float poison = bad ? NAN : 1.0f;
+    const bool hok = head < H;
+    float a0 = 0.0f, a1 = 0.0f, lsum = 1.0f;
+#pragma unroll
+    for (int r = 0; r < 2; r++) {
+        // Round 0: every wave is past its value products (the buffer is free).
+        // Round 1: every partner has read round 0.
+        lds_barrier();
+#pragma unroll
+        for (int i = 0; i < HALF; i++) xch[(w * HALF + i) * 64 + lane] = acc[OWN * (1 - KH) + r * HALF + i];
+        lds_barrier();
+        if (r == 0) {
+            const int p = w ^ 4;
+            const float mp = meta[p][0][l16], rp = meta[p][1][l16], lp = meta[p][2][l16];
+            const float m0 = KH ? mp : st.m, r0 = KH ? rp : st.ref, l0 = KH ? lp : st.l;
+            const float m1 = KH ? st.m : mp, r1 = KH ? st.ref : rp, l1 = KH ? st.l : lp;
+            const float R = m0 >= m1 ? r0 : r1;
+            a0 = l0 == 0.0f ? 0.0f : exp2_hw(r0 - R);
+            a1 = l1 == 0.0f ? 0.0f : exp2_hw(r1 - R);
+            // Explicit fused forms: the order of the two products is fixed, whatever
+            // contraction the compiler would choose in each instance.
+            lsum = __builtin_fmaf(a0, l0, a1 * l1);
+        }
+#pragma unroll
+        for (int i = 0; i < HALF; i++) {
+            const int cb = OWN * KH + r * HALF + i;
+            const f32x4 own = acc[cb];
+            const f32x4 par = xch[((w ^ 4) * HALF + i) * 64 + lane];
+            const f32x4 x0 = KH ? par : own;
+            const f32x4 x1 = KH ? own : par;
+            f32x4 o;
+#pragma unroll
+            for (int e = 0; e < 4; e++) o[e] = (__builtin_fmaf(a0, x0[e], a1 * x1[e]) / lsum) * poison;
+            const int off = hok ? (head * kHeadDim + col0 + 16 * cb) * 4 : kDropOffset;
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o), rsrc, off, 0, kStoreNT);
+        }
+    }
+}
+
+// Work items shared by both kernels. A unit is one (query row, head group of 64, column
+// slice); a workgroup serves units base, base + G, ... as one stream of 64-key tiles (at
+// least one per unit; a row with no selected key runs one all-masked tile, which changes
+// nothing). useq counts the units this workgroup has started, to tell whose bad-index
+// flag a resolved list belongs to.
+struct Item {              // all fields wave-uniform
+    int64_t unit;          // < 0: none
+    int64_t row;
+    int tile, ntiles, n, hg, cs, useq;
+};
+
+template <int NS>
+struct Stream {
+    const AttnArgs &a;
+    int n_hg;
+    int64_t units, G;
+    __device__ Item make(int64_t u, int useq) const {
+        Item it{};
+        it.unit = u;
+        it.useq = useq;
+        if (u < 0 || u >= units) { it.unit = -1; return it; }
+        it.cs = (int)(u % NS);
+        it.hg = (int)((u / NS) % n_hg);
+        it.row = u / ((int64_t)NS * n_hg);
+        // A scalar (constant address space) load: it waits on the LDS/scalar counter, not
+        // on the vector-memory counter that the in-flight gathers hold.
+        int n = a.nsel ? *(const __attribute__((address_space(4))) int32_t *)(a.nsel + it.row) : a.kmax;
+        n = n < 0 ? 0 : (n > a.kmax ? a.kmax : n);
+        it.n = n;
+        it.tile = 0;
+        it.ntiles = n > 0 ? (n + kTile - 1) / kTile : 1;
+        return it;
+    }
+    __device__ Item next(const Item &it) const {
+        if (it.unit < 0) return it;
+        if (it.tile + 1 < it.ntiles) { Item nx = it; nx.tile++; return nx; }
+        return make(it.unit + G, it.useq + 1);
+    }
+};
+
+// Index list of an item's tile into one of this wave's LDS slots: lane l fetches entry
+// tile*64 + l (address clamped to the row). Always issued, also when there is no item (then
+// the fallback's list is re-read), so that every wave issues the same number of
+// vector-memory operations per tile.
+__device__ __forceinline__ void dma_idx(const AttnArgs &a, const Item &it, const Item &fallback, int *slot, int lane) {
+    const Item &src = it.unit >= 0 ? it : fallback;
+    const int p = (it.unit >= 0 ? it.tile : 0) * kTile + lane;
+    const int pc = p < a.kmax ? p : a.kmax - 1;
+    dma4(a.idx + src.row * a.kmax, (uint32_t)pc * 4u, lds_addr(slot));
+}
+// Row to gather for entry tile*64 + l, or -1 (masked or out of range: gather zeros); bad is
+// set when a live entry (inside the row's count) is out of range.
+__device__ __forceinline__ int resolve(const AttnArgs &a, const Item &it, const int *slot, int lane, bool &bad) {
+    const int iv = slot[lane];
+    const int p = it.tile * kTile + lane;
+    const bool live = p < it.n;
+    const bool inr = iv >= 0 && (int64_t)iv < a.n_ctx;
+    bad = __builtin_amdgcn_ballot_w64(live && !inr) != 0;
+    return (live && inr) ? iv : -1;
+}
+
+// The next unit's query and sink, loaded asynchronously into qreg (the previous unit's last
+// scores have been formed by then); usable after a wait that covers them and register_ready.
+// Lane (g, l16) holds head l16 of the wave's 16, dims 32kk + 8g + 0..7 for kk < 16. Heads
+// past H read zeros (query and sink) from the static zero row.
+__device__ __forceinline__ void load_q_async(const AttnArgs &a, const Item &it, int hq, int g, int l16,
+                                             bf16x8 (&qreg)[16], float &sink) {
+    const int head = it.hg * 64 + 16 * hq + l16;
+    const bool ok = head < a.H;
+    const uint16_t *qrow =
+        ok ? (const uint16_t *)a.q + (it.row * a.H + head) * kHeadDim : (const uint16_t *)g_zero_row;
+    qrow += 8 * g;
+#pragma unroll
+    for (int kk = 0; kk < 16; kk++) load16_async(qreg[kk], qrow + 32 * kk);
+    load4_async(sink, ok ? a.sinks + head : (const float *)g_zero_row);
+}
+__device__ __forceinline__ void q_ready(bf16x8 (&qreg)[16], float &sink) {
+#pragma unroll
+    for (int kk = 0; kk < 16; kk++) register_ready(qreg[kk]);
+    register_ready(sink);
+}
+
+// ---------------------------------------------------------------------------------------
+// Separate K and V caches. One K buffer and one V buffer of 64 rows each: V(j) is gathered
+// while the scores of tile j run, K(j+1) while its values are applied. Two barriers per
+// tile: "K(j) landed, V buffer free" and "V(j) landed, K buffer free".
+template <int NS>
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+attn_bf16_ks_kernel(AttnArgs a, int n_hg, int64_t units) {
+    constexpr int COLS = kHeadDim / NS;        // output columns per workgroup
+    constexpr int CB = COLS / 16;              // 16-column blocks of the value MFMA
+    constexpr int VROW = COLS * 2;             // bytes of one V row slice
+    constexpr int VSTRIDE = vstride_of(VROW);
+    constexpr int VCHUNKS = VROW / 16;         // 16-byte pieces of a V row slice
+    constexpr int kStores = CB / 2;            // output stores per wave per unit
+    static_assert(kRows == 8 && CB >= 4, "tile split");
+    static_assert(kWaves * (CB / 4) * 1024 <= kTile * VSTRIDE, "the exchange fits the V buffer");
+    static_assert(kStores + kRows < 64, "vmcnt range");
+
+    __shared__ __attribute__((aligned(16))) char k_lds[kTile * kKStride];
+    __shared__ __attribute__((aligned(16))) char v_lds[kTile * VSTRIDE];
+    __shared__ int idx_lds[kWaves][2][64];   // each wave's own copy of a tile's index list
+    __shared__ float meta_lds[kWaves][3][16];
+
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int g = lane >> 4;
+    const int l16 = lane & 15;
+    const int hq = w & 3;
+    const int kh = w >> 2;
+    const Stream<NS> str{a, n_hg, units, (int64_t)gridDim.x};
+
+    // Wave w gathers tile keys 8w .. 8w+7 (all in its own key half) into both buffers: key
+    // 32kh + kap goes to K slot 32kh + kslot_of_key(kap) and to V slot 32kh + swap23(kap).
+    // One DMA instruction moves one cache row (64 lanes x 16 bytes) or its column slice. The
+    // buffer resource spans the row's cache; a masked key (-1) has a wrapped-around offset
+    // past its end and arrives as zeros.
+    auto rsrc_k = [&](const Item &it) {
+        return __builtin_amdgcn_make_buffer_rsrc((void *)((const char *)a.k + it.row * a.cache_stride * 2), 0,
+                                                 (int)(uint32_t)(a.n_ctx * kRowBytes), kBufferFlags);
+    };
+    auto rsrc_v = [&](const Item &it) {
+        return __builtin_amdgcn_make_buffer_rsrc(
+            (void *)((const char *)a.v + it.row * a.cache_stride * 2 + (int64_t)it.cs * VROW), 0,
+            (int)(uint32_t)(a.n_ctx * kRowBytes - (int64_t)it.cs * VROW), kBufferFlags);
+    };
+    auto dma_k_row = [&](__amdgpu_buffer_rsrc_t rsrc, int iv, int i) {
+        const int ij = __builtin_amdgcn_readlane(iv, kRows * w + i);
+        const int slot = 32 * kh + kslot_of_key(8 * hq + i);
+        dma16_buf(rsrc, ((uint32_t)ij << 10) + ((uint32_t)lane << 4), lds_addr((SA_LDS char *)k_lds + slot * kKStride));
+    };
+    auto dma_v_row = [&](__amdgpu_buffer_rsrc_t rsrc, int iv, int i) {
+        const int ij = __builtin_amdgcn_readlane(iv, kRows * w + i);
+        const int slot = 32 * kh + swap23(8 * hq + i);
+        if (VCHUNKS == 64 || lane < VCHUNKS)
+            dma16_buf(rsrc, ((uint32_t)ij << 10) + ((uint32_t)lane << 4), lds_addr((SA_LDS char *)v_lds + slot * VSTRIDE));
+    };
+
+    const float scale2 = a.scale * kLog2e;
+    bf16x8 qreg[16];
+    f32x4 acc[CB];       // head l16, columns 16cb + 4g + 0..3 of the slice
+    HalfState st;
+    float sink_n;
+
+    // Issue order per wave: Q/sink(0), I(0) | drain | K(0), I(1); then in tile j: V(j)
+    // spread through the scores; on a unit's last tile the next unit's query and sink
+    // (kQLoads) once V(j) has landed; K(j+1) spread through the values; then I(j+2),
+    // followed on a unit's last tile by its kStores output stores. Each wait below counts
+    // exactly the operations issued after the one it needs.
+    Item cur = str.make(xcd_remap(blockIdx.x, str.G), 0);
+    Item nx = str.next(cur);
+    Item nx2 = str.next(nx);
+    bool bad = false, bad_next = false;
+    load_q_async(a, cur, hq, g, l16, qreg, sink_n);
+    dma_idx(a, cur, cur, &idx_lds[w][0][0], lane);
+    wait_vmcnt<0>();
+    q_ready(qreg, sink_n);
+    half_start(st, acc, kh == 0, sink_n);
+    __builtin_amdgcn_s_waitcnt(0);  // nothing the compiler tracks is pending in the loop
+    bool starting = false;          // the next unit's query is in flight; its stores follow I(j+1)
+    int iv_cur = resolve(a, cur, &idx_lds[w][0][0], lane, bad);
+    {
+        const __amdgpu_buffer_rsrc_t rk = rsrc_k(cur);
+#pragma unroll
+        for (int i = 0; i < kRows; i++) dma_k_row(rk, iv_cur, i);
+        dma_idx(a, nx, cur, &idx_lds[w][1][0], lane);
+    }
+
+    // Per-lane LDS read bases. Scores: slot 32kh + 16b + l16, dims 32kk + 8g + 0..7.
+    const SA_LDS char *krow = (const SA_LDS char *)k_lds + (32 * kh + l16) * kKStride + 16 * g;
+    // Values: lane (g, l16) addresses the V slot of key 8g + 4t2 + l16/4 of its half and
+    // columns 16cb + 4(l16%4) .. +3; the transposing read returns column 16cb + l16 of keys
+    // 8g + 4t2 + 0..3, which are elements 4t2 + 0..3 of the V^T operand.
+    const SA_LDS char *vrow =
+        (const SA_LDS char *)v_lds + (32 * kh + swap23(8 * g + (l16 >> 2))) * VSTRIDE + 8 * (l16 & 3);
+
+    for (int j = 0; cur.unit >= 0; j++) {
+        const bool more = nx.unit >= 0;
+        const bool last_of_unit = !more || nx.unit != cur.unit;
+        // K(j) has landed for this wave, and with it a unit's query and sink when tile j
+        // starts one. After K(j) come I(j+1) and, when tile j starts a unit, the previous
+        // unit's stores.
+        if (starting) wait_vmcnt<vm_clamp(1 + kStores)>(); else wait_vmcnt<1>();
+        if (starting) {
+            q_ready(qreg, sink_n);
+            half_start(st, acc, kh == 0, sink_n);
+        }
+        lds_barrier();  // every wave's K(j) has landed; every wave is done with V(j-1)
+
+        // ---- scores of the wave's 32 keys for its 16 heads over the full head width.
+        f32x4 sacc0 = (f32x4){}, sacc1 = (f32x4){};
+        {
+            const __amdgpu_buffer_rsrc_t rv = rsrc_v(cur);
+            bf16x8 k0 = *(const SA_LDS bf16x8 *)(krow);
+            bf16x8 k1 = *(const SA_LDS bf16x8 *)(krow + 16 * kKStride);
+#pragma unroll
+            for (int kk = 0; kk < 16; kk++) {
+                bf16x8 n0 = k0, n1 = k1;
+                if (kk + 1 < 16) {
+                    n0 = *(const SA_LDS bf16x8 *)(krow + 64 * (kk + 1));
+                    n1 = *(const SA_LDS bf16x8 *)(krow + 16 * kKStride + 64 * (kk + 1));
+                }
+                sacc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qreg[kk], sacc0, 0, 0, 0);
+                sacc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qreg[kk], sacc1, 0, 0, 0);
+                // The tile's V rows go out here, one every two steps, in the matrix pipe's
+                // shadow (every wave finished the previous tile's values before the barrier).
+                if (kk % 2 == 0) dma_v_row(rv, iv_cur, kk / 2);
+                __builtin_amdgcn_sched_barrier(0);
+                k0 = n0;
+                k1 = n1;
+            }
+        }
+
+        // Indices of item j+1 have landed (after them: [stores], V(j)).
+        if (starting) wait_vmcnt<vm_clamp(kStores + kRows)>(); else wait_vmcnt<kRows>();
+        starting = false;
+        int iv_n = 0;
+        const bool q_now = last_of_unit && more;
+        if (more) {
+            bool b;
+            iv_n = resolve(a, nx, &idx_lds[w][(j + 1) & 1][0], lane, b);
+            if (nx.unit == cur.unit) bad = bad || b; else bad_next = bad_next || b;
+        }
+
+        bf16x8 ph, pl;
+        half_tile(sacc0, sacc1, cur.tile * kTile + 32 * kh + 8 * g, cur.n, scale2, st, acc, ph, pl);
+
+        // V(j) has landed: nothing was issued after it.
+        wait_vmcnt<0>();
+        // On a unit's last tile: the next unit's query (the scores were qreg's last use),
+        // ahead of the K rows, so the wait for K(j+1) covers it too.
+        if (q_now) load_q_async(a, nx, hq, g, l16, qreg, sink_n);
+        lds_barrier();  // every wave's V(j) has landed; every wave is done with K(j)
+
+        // ---- values O^T += V^T P^T over the wave's 32 keys, one MFMA per part of P.
+        {
+            const __amdgpu_buffer_rsrc_t rk = rsrc_k(nx);
+            auto read_v = [&](int cb) -> bf16x8 {
+                const bf16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((SA_LDS bf16x4 *)(vrow + 32 * cb));
+                const bf16x4 t1 =
+                    __builtin_amdgcn_ds_read_tr16_b64_v4bf16((SA_LDS bf16x4 *)(vrow + 8 * VSTRIDE + 32 * cb));
+                return (bf16x8){t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3]};
+            };
+            bf16x8 vcur = read_v(0);
+#pragma unroll
+            for (int cb = 0; cb < CB; cb++) {
+                bf16x8 vnxt = vcur;
+                if (cb + 1 < CB) vnxt = read_v(cb + 1);
+                acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vcur, ph, acc[cb], 0, 0, 0);
+                acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vcur, pl, acc[cb], 0, 0, 0);
+                // The next tile's K rows go out here, in the matrix pipe's shadow (every
+                // wave is past this tile's scores: the K buffer is free).
+                if (more) {
+#pragma unroll
+                    for (int r = cb * kRows / CB; r < (cb + 1) * kRows / CB; r++) dma_k_row(rk, iv_n, r);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                vcur = vnxt;
+            }
+        }
+
+        dma_idx(a, nx2, cur, &idx_lds[w][j & 1][0], lane);  // slot j&1 held item j's list
+        iv_cur = iv_n;
+        starting = q_now;
+        if (last_of_unit) {
+            float *orow = a.out + cur.row * a.H * kHeadDim;
+            const int head = cur.hg * 64 + 16 * hq + l16;
+            const int col0 = cur.cs * COLS + 4 * g;
+            f32x4 *xch = (f32x4 *)v_lds;
+            if (kh) combine_store<1>(st, acc, meta_lds, xch, w, lane, g, l16, orow, a.H, head, col0, bad);
+            else combine_store<0>(st, acc, meta_lds, xch, w, lane, g, l16, orow, a.H, head, col0, bad);
+            bad = bad_next;
+            bad_next = false;
+        }
+        cur = nx;
+        nx = nx2;
+        nx2 = str.next(nx2);
+    }
+    wait_vmcnt<0>();
+}
+
+// ---------------------------------------------------------------------------------------
+// One cache as K and V. Two tile buffers of 64 full rows alternate: tile j+1 is gathered
+// during all of tile j (half of its rows in the scores, half in the values), and one
+// barrier per tile hands buffers over ("T(j) landed; every wave is done with tile j-1, so
+// its buffer may be refilled"). Index lists run two tiles ahead of the compute. Rows are
+// stored with stride 1024 and the chunk swizzle tswz (applied on the gather side: lane i
+// of a row's DMA fetches chunk i ^ tswz(slot)), and the LDS reads undo it by XOR.
+template <int NS>
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+attn_bf16_ks_alias_kernel(AttnArgs a, int n_hg, int64_t units) {
+    constexpr int COLS = kHeadDim / NS;
+    constexpr int CB = COLS / 16;
+    constexpr int kStores = CB / 2;
+    constexpr int kTileBytes = kTile * kRowBytes;
+    static_assert(kRows == 8 && CB >= 4, "tile split");
+    static_assert(kWaves * (CB / 4) * 1024 <= kTileBytes, "the exchange fits a tile buffer");
+
+    __shared__ __attribute__((aligned(1024))) char t_lds[2 * kTileBytes];
+    __shared__ int idx_lds[kWaves][2][64];
+    __shared__ float meta_lds[kWaves][3][16];
+
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int g = lane >> 4;
+    const int l16 = lane & 15;
+    const int hq = w & 3;
+    const int kh = w >> 2;
+    const Stream<NS> str{a, n_hg, units, (int64_t)gridDim.x};
+    const uint32_t t_base = lds_addr((SA_LDS char *)t_lds);
+
+    auto rsrc_t = [&](const Item &it) {
+        if (it.unit < 0) return __builtin_amdgcn_make_buffer_rsrc((void *)a.k, 0, 0, kBufferFlags);
+        return __builtin_amdgcn_make_buffer_rsrc((void *)((const char *)a.k + it.row * a.cache_stride * 2), 0,
+                                                 (int)(uint32_t)(a.n_ctx * kRowBytes), kBufferFlags);
+    };
+    // Wave w gathers tile keys 8w .. 8w+7 of its key half into K slots (as the separate
+    // kernel's K buffer), whole rows, swizzled.
+    auto dma_t_row = [&](__amdgpu_buffer_rsrc_t rsrc, int iv, int buf, int i) {
+        const int ij = __builtin_amdgcn_readlane(iv, kRows * w + i);
+        const int slot = 32 * kh + kslot_of_key(8 * hq + i);
+        const uint32_t src_chunk = (uint32_t)(lane ^ tswz(slot));
+        dma16_buf(rsrc, ((uint32_t)ij << 10) + (src_chunk << 4), t_base + buf * kTileBytes + slot * kRowBytes);
+    };
+
+    const float scale2 = a.scale * kLog2e;
+    bf16x8 qreg[16];
+    f32x4 acc[CB];
+    HalfState st;
+    float sink_n;
+
+    // Read bases within a buffer (XOR with the per-step column offset; bits 4-9 only).
+    // Scores: slot 32kh + 16b + l16, chunk 4kk + g, stored at (4kk + g) ^ tswz(l16).
+    const uint32_t kbase = (uint32_t)((32 * kh + l16) * kRowBytes + 16 * (g ^ tswz(l16)));
+    // Values: lane (g, l16) reads the slot of key 8g + 4t2 + l16/4 of its half, which is
+    // K slot 16t2 + 4g + l16/4, columns 16cb + 4(l16%4) .. +3: chunk 2cb + h (h = (l16%4)/2),
+    // stored at (2cb + h) ^ tswz(slot), plus 8 bytes for odd l16.
+    const int vslot = 32 * kh + 4 * g + (l16 >> 2);
+    const uint32_t vbase =
+        (uint32_t)(vslot * kRowBytes + 8 * (l16 & 1) + 16 * (((l16 & 3) >> 1) ^ tswz(vslot)));
+
+    // Issue order per wave: Q/sink(0), I(0), I(1) | drain | T(0), I(2); then in tile j:
+    // half of T(j+1) through the scores, on a unit's last tile the next unit's query and
+    // sink (kQLoads), the rest of T(j+1) through the values, then I(j+3) and on a unit's
+    // last tile its kStores output stores.
+    Item cur = str.make(xcd_remap(blockIdx.x, str.G), 0);
+    Item nx = str.next(cur);
+    Item nx2 = str.next(nx);
+    bool bad0 = false, bad1 = false, bad2 = false;  // units cur.useq, +1, +2
+    int cur_useq = 0;
+    auto note_bad = [&](const Item &it, bool b) {
+        const int d = it.useq - cur_useq;
+        bad0 = bad0 || (b && d == 0);
+        bad1 = bad1 || (b && d == 1);
+        bad2 = bad2 || (b && d == 2);
+    };
+    load_q_async(a, cur, hq, g, l16, qreg, sink_n);
+    dma_idx(a, cur, cur, &idx_lds[w][0][0], lane);
+    dma_idx(a, nx, cur, &idx_lds[w][1][0], lane);
+    wait_vmcnt<0>();
+    q_ready(qreg, sink_n);
+    half_start(st, acc, kh == 0, sink_n);
+    __builtin_amdgcn_s_waitcnt(0);
+    int iv_next = 0;  // rows of the tile after the current one
+    {
+        bool b;
+        const int iv0 = resolve(a, cur, &idx_lds[w][0][0], lane, b);
+        note_bad(cur, b);
+        if (nx.unit >= 0) {
+            iv_next = resolve(a, nx, &idx_lds[w][1][0], lane, b);
+            note_bad(nx, b);
+        }
+        const __amdgpu_buffer_rsrc_t rt = rsrc_t(cur);
+#pragma unroll
+        for (int i = 0; i < kRows; i++) dma_t_row(rt, iv0, 0, i);
+        dma_idx(a, nx2, cur, &idx_lds[w][0][0], lane);
+    }
+    bool starting = false;      // tile j starts a unit whose query was loaded in tile j-1
+    bool stores_prev = false;   // tile j-1 ended a unit: its stores follow I(j+2)
+
+    for (int j = 0; cur.unit >= 0; j++) {
+        const int buf = j & 1;
+        const bool more = nx.unit >= 0;
+        const bool last_of_unit = !more || nx.unit != cur.unit;
+        const bool q_now = last_of_unit && more;
+        // T(j) has landed for this wave (and the query, issued before its last rows).
+        // After T(j) come I(j+2) and, when tile j-1 ended a unit, its stores.
+        if (stores_prev) wait_vmcnt<vm_clamp(1 + kStores)>(); else wait_vmcnt<1>();
+        if (starting) {
+            q_ready(qreg, sink_n);
+            half_start(st, acc, kh == 0, sink_n);
+        }
+        lds_barrier();  // every wave's T(j) has landed; every wave is done with tile j-1
+
+        const uint32_t tb = t_base + buf * kTileBytes;
+        const __amdgpu_buffer_rsrc_t rt = rsrc_t(nx);
+        // ---- scores of the wave's 32 keys for its 16 heads over the full head width.
+        f32x4 sacc0 = (f32x4){}, sacc1 = (f32x4){};
+        {
+            const uint32_t kb = tb + kbase;
+            bf16x8 k0 = *lds_at<bf16x8>(kb);
+            bf16x8 k1 = *lds_at<bf16x8>(kb + 16 * kRowBytes);
+#pragma unroll
+            for (int kk = 0; kk < 16; kk++) {
+                bf16x8 n0 = k0, n1 = k1;
+                if (kk + 1 < 16) {
+                    n0 = *lds_at<bf16x8>(kb ^ (64u * (kk + 1)));
+                    n1 = *lds_at<bf16x8>((kb ^ (64u * (kk + 1))) + 16 * kRowBytes);
+                }
+                sacc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qreg[kk], sacc0, 0, 0, 0);
+                sacc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qreg[kk], sacc1, 0, 0, 0);
+                // Rows 0..3 of T(j+1), one every four steps.
+                if (more && kk % 4 == 0) dma_t_row(rt, iv_next, buf ^ 1, kk / 4);
+                __builtin_amdgcn_sched_barrier(0);
+                k0 = n0;
+                k1 = n1;
+            }
+        }
+        // The scores were the last use of qreg in this unit.
+        if (q_now) load_q_async(a, nx, hq, g, l16, qreg, sink_n);
+
+        bf16x8 ph, pl;
+        half_tile(sacc0, sacc1, cur.tile * kTile + 32 * kh + 8 * g, cur.n, scale2, st, acc, ph, pl);
+
+        // ---- values O^T += V^T P^T over the wave's 32 keys, one MFMA per part of P.
+        {
+            const uint32_t vb = tb + vbase;
+            const uint32_t cbase = (uint32_t)(cur.cs * COLS * 2);
+            auto read_v = [&](int cb) -> bf16x8 {
+                const uint32_t ad = vb ^ (cbase + 32u * cb);
+                const bf16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((SA_LDS bf16x4 *)lds_at<bf16x4>(ad));
+                const bf16x4 t1 =
+                    __builtin_amdgcn_ds_read_tr16_b64_v4bf16((SA_LDS bf16x4 *)lds_at<bf16x4>(ad + 16 * kRowBytes));
+                return (bf16x8){t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3]};
+            };
+            bf16x8 vcur = read_v(0);
+#pragma unroll
+            for (int cb = 0; cb < CB; cb++) {
+                bf16x8 vnxt = vcur;
+                if (cb + 1 < CB) vnxt = read_v(cb + 1);
+                acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vcur, ph, acc[cb], 0, 0, 0);
+                acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vcur, pl, acc[cb], 0, 0, 0);
+                // Rows 4..7 of T(j+1).
+                if (more) {
+#pragma unroll
+                    for (int r = cb * 4 / CB; r < (cb + 1) * 4 / CB; r++) dma_t_row(rt, iv_next, buf ^ 1, 4 + r);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                vcur = vnxt;
+            }
+        }
+
+        // Indices of item j+2 have landed: after I(j+2) came [stores of tile j-1's unit],
+        // T(j+1) (when there is a tile j+1) and [the next unit's query].
+        if (nx2.unit >= 0) {
+            wait_vmcnt_dyn((stores_prev ? kStores : 0) + (more ? kRows : 0) + (q_now ? kQLoads : 0));
+            bool b;
+            iv_next = resolve(a, nx2, &idx_lds[w][buf][0], lane, b);
+            note_bad(nx2, b);
+        }
+        const Item nx3 = str.next(nx2);
+        dma_idx(a, nx3, cur, &idx_lds[w][buf ^ 1][0], lane);  // slot buf^1 held I(j+1)
+        stores_prev = last_of_unit;
+        starting = q_now;
+        if (last_of_unit) {
+            float *orow = a.out + cur.row * a.H * kHeadDim;
+            const int head = cur.hg * 64 + 16 * hq + l16;
+            const int col0 = cur.cs * COLS + 4 * g;
+            f32x4 *xch = (f32x4 *)(t_lds + buf * kTileBytes);
+            if (kh) combine_store<1>(st, acc, meta_lds, xch, w, lane, g, l16, orow, a.H, head, col0, bad0);
+            else combine_store<0>(st, acc, meta_lds, xch, w, lane, g, l16, orow, a.H, head, col0, bad0);
+            bad0 = bad1;
+            bad1 = bad2;
+            bad2 = false;
+            cur_useq++;
+        }
+        cur = nx;
+        nx = nx2;
+        nx2 = nx3;
+    }
+    wait_vmcnt<0>();
+}
+
+template <int NS, bool ALIAS>
+hipError_t launch_ks(const AttnArgs &a, int64_t units, int64_t grid, hipStream_t s) {
+    const int n_hg = (a.H + 63) / 64;
+    if (ALIAS)
+        hipLaunchKernelGGL((attn_bf16_ks_alias_kernel<NS>), dim3((unsigned)grid), dim3(512), 0, s, a, n_hg, units);
+    else
+        hipLaunchKernelGGL((attn_bf16_ks_kernel<NS>), dim3((unsigned)grid), dim3(512), 0, s, a, n_hg, units);
+    return hipGetLastError();
+}
+
+template <bool ALIAS>
+hipError_t launch_ks_cols(const AttnArgs &a, int cols, int64_t units, hipStream_t s) {
+    const int64_t cus = device_cu_count();
+    const int64_t grid = units < cus ? units : cus;
+    switch (cols) {
+        case 512: return launch_ks<1, ALIAS>(a, units, grid, s);
+        case 256: return launch_ks<2, ALIAS>(a, units, grid, s);
+        case 128: return launch_ks<4, ALIAS>(a, units, grid, s);
+        case 64: return launch_ks<8, ALIAS>(a, units, grid, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+int attn_bf16_ks_lds_bytes(int cols, bool alias) {
+    const int small = kWaves * 2 * 64 * 4 + kWaves * 3 * 16 * 4;
+    if (alias) return 2 * kTile * kRowBytes + small;
+    return kTile * kKStride + kTile * vstride_of(cols * 2) + small;
+}
+
+hipError_t launch_attn_bf16_ks(const AttnArgs &a, int cols, int64_t units, hipStream_t s) {
+    return a.k == a.v ? launch_ks_cols<true>(a, cols, units, s) : launch_ks_cols<false>(a, cols, units, s);
+}
+
+}  // namespace sa

@@ -53,6 +53,24 @@ __device__ __forceinline__ void wait_vmcnt() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// s_waitcnt vmcnt(n) for a wave-uniform n formed at run time (clamped to 0..63; a
+// smaller count only waits longer).
+__device__ __forceinline__ void wait_vmcnt_dyn(int n) {
+    n = n < 0 ? 0 : (n > 63 ? 63 : n);
+    switch (__builtin_amdgcn_readfirstlane(n)) {
+#define SA_W(N) case N: wait_vmcnt<N>(); break;
+        SA_W(0) SA_W(1) SA_W(2) SA_W(3) SA_W(4) SA_W(5) SA_W(6) SA_W(7) SA_W(8) SA_W(9)
+        SA_W(10) SA_W(11) SA_W(12) SA_W(13) SA_W(14) SA_W(15) SA_W(16) SA_W(17) SA_W(18) SA_W(19)
+        SA_W(20) SA_W(21) SA_W(22) SA_W(23) SA_W(24) SA_W(25) SA_W(26) SA_W(27) SA_W(28) SA_W(29)
+        SA_W(30) SA_W(31) SA_W(32) SA_W(33) SA_W(34) SA_W(35) SA_W(36) SA_W(37) SA_W(38) SA_W(39)
+        SA_W(40) SA_W(41) SA_W(42) SA_W(43) SA_W(44) SA_W(45) SA_W(46) SA_W(47) SA_W(48) SA_W(49)
+        SA_W(50) SA_W(51) SA_W(52) SA_W(53) SA_W(54) SA_W(55) SA_W(56) SA_W(57) SA_W(58) SA_W(59)
+        SA_W(60) SA_W(61) SA_W(62)
+#undef SA_W
+        default: wait_vmcnt<63>(); break;
+    }
+}
+
 // Workgroup barrier for LDS traffic only: outstanding LDS operations complete,
 // in-flight DMA gathers stay in flight.
 __device__ __forceinline__ void lds_barrier() {
@@ -112,6 +130,18 @@ __device__ __forceinline__ float max_xor32(float x) {
 }
 __device__ __forceinline__ float sum_xor32(float x) {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// The same over lanes l and l ^ 16 with v_permlane16_swap: it hands rows 1 and 3 of the
+// wave (16 lanes each) their even neighbour's values and the reverse, so the two results
+// are the pair's values in some order, and a sum of the two is the same in both lanes.
+__device__ __forceinline__ float max_xor16(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor16(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 

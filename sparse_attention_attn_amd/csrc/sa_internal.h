@@ -39,6 +39,11 @@ hipError_t launch_attn_bf16(const AttnArgs &a, hipStream_t s);
 // selected row is gathered once.
 hipError_t launch_attn_bf16_alias(const AttnArgs &a, hipStream_t s);
 hipError_t launch_attn_f32(const AttnArgs &a, hipStream_t s);
+// The eight-wave kernels for blocks of 64 heads and cols = 512, 256, 128 or 64 output
+// columns per workgroup (sa_attn_ks.hip; the aliased one when a.k == a.v), and their
+// static LDS size.
+hipError_t launch_attn_bf16_ks(const AttnArgs &a, int cols, int64_t units, hipStream_t s);
+int attn_bf16_ks_lds_bytes(int cols, bool alias);
 hipError_t launch_topk(const TopkArgs &a, hipStream_t s);
 hipError_t launch_pad_heads(int dtype, const void *q, int64_t rows, int h_real, int h_pad,
                             const float *sinks, void *q_pad, float *sinks_pad, hipStream_t s);

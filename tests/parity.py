@@ -60,7 +60,10 @@ def to_device(case, device):
 
     k = case.k[0] if case.shared_cache else case.k
     v = case.v[0] if case.shared_cache else case.v
-    return {"q": t(case.q), "k": t(k), "v": t(v),
+    kt = t(k)
+    # A case whose V is its K array runs on one device tensor (the aliased-cache path).
+    vt = kt if case.v is case.k else t(v)
+    return {"q": t(case.q), "k": kt, "v": vt,
             "idx": torch.from_numpy(np.ascontiguousarray(case.idx, dtype=np.int32)).to(device),
             "nsel": torch.from_numpy(np.ascontiguousarray(case.nsel, dtype=np.int32)).to(device),
             "sinks": torch.from_numpy(np.ascontiguousarray(case.sinks, dtype=np.float32)).to(device)}

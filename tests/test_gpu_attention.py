@@ -192,6 +192,23 @@ def test_sink_minus_inf_empty_row_is_nan():
     assert np.all(np.isnan(got[1]))
 
 
+@pytest.mark.parametrize("heads,alias", [(32, False), (64, False), (64, True)])
+def test_sink_minus_inf_scores_far_below_zero(heads, alias):
+    """Heads whose sink is -inf and whose every score lies near -250: the first tile moves the
+    exponent reference from 0 down to the maximum, with nothing accumulated yet. The result
+    is an ordinary weighted average (the oracle's), not inf * 0."""
+    rng = np.random.default_rng(53)
+    c = w.decode_bf16(seed=53, batch=3, heads=heads, n_ctx=300, k=130)
+    c.q[:] = 0x3F80                                   # 1.0
+    c.k[:] = rng.choice(np.array([0xBF00, 0xBE80, 0xBF40], dtype=np.uint16), size=c.k.shape)  # -0.5, -0.25, -0.75
+    if alias:
+        c.v = c.k
+    c.scale = 1.0
+    c.sinks[: heads // 2] = -np.inf
+    got, ref = check_case(c, label=f"sink -inf, scores ~ -250, H={heads}{' aliased' if alias else ''}")
+    assert np.all(np.isfinite(got))
+
+
 def test_determinism_and_guards():
     """Five repeats are byte-identical and never write outside their output."""
     import sparse_attention_attn_amd as sa
