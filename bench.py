@@ -61,7 +61,7 @@ def algorithmic_flops(rows: int, heads: int, d: int, k: int) -> int:
 
 
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "attn_decode_b1024_h64_k640_hbm_traffic.md")
-KERNEL_SOURCE = os.path.join(ROOT, "sparse_attention_attn_amd", "csrc", "sa_attn.hip")
+KERNEL_SOURCE = os.path.join(ROOT, "sparse_attention_attn_amd", "csrc", "sa_attn_ks.hip")
 
 
 def measured_traffic(rows: int, heads: int, n_ctx: int, k: int):
@@ -253,8 +253,8 @@ def main() -> int:
             "unit": "GB/s",
             "frac": achieved_gbs / HBM_PEAK_GBS,
             "traffic": None if alias else measured_traffic(B, H, N, K),
-            "kernel": "attn_bf16_alias_kernel<2,8> (sparse_attn_decode, K = V)" if alias
-                      else "attn_bf16_kernel<2,8> (sparse_attn_decode)",
+            "kernel": "attn_bf16_ks_alias_kernel<1> (sparse_attn_decode, K = V)" if alias
+                      else "attn_bf16_ks_kernel<1> (sparse_attn_decode)",
             "kernel_ms": attn_ms,
             "algorithmic_bytes_per_launch": nbytes,
             "mfma_tflops": flops / (attn_ms * 1e-3) / 1e12,
@@ -401,7 +401,7 @@ def bench_prefill(args, torch, sa, w, dev) -> int:
         "roofline": {
             "bound": "mfma", "achieved": tflops, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": tflops / MFMA_BF16_PEAK_TFLOPS, "traffic": None,
-            "kernel": f"attn_bf16_kernel<{2 if h_launch > 32 else 1},8> (sparse_attn_prefill)",
+            "kernel": ("attn_bf16_ks_kernel<1>" if h_launch > 32 else "attn_bf16_kernel<1,8>") + " (sparse_attn_prefill)",
             "kernel_ms": attn_ms, "algorithmic_flops_per_launch": flops,
             "gathered_bytes_per_launch": gathered, "gathered_gbs": gathered / (attn_ms * 1e-3) / 1e9,
             "unique_hbm_bytes_per_launch": unique,

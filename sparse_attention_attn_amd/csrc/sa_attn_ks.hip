@@ -157,17 +157,25 @@ __device__ __forceinline__ void half_tile(const f32x4 &s0, const f32x4 &s1, int 
     }
 }
 
+// Row rotation by 8 inside each 16-lane row (DPP row_ror:8): lane l16 receives lane l16 ^ 8.
+__device__ __forceinline__ float ror8(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xf, 0xf, false));
+}
+
 // End of a unit: combine the two key halves and store. The pair (w, w ^ 4) holds the same
 // heads; wave kh finalises column blocks OWN*kh .. OWN*kh + OWN-1 in two rounds of OWN/2.
 // Per round each wave writes the partner's blocks (16-byte pieces, lane-major) into its
 // slot of xch (a free gathered buffer) and reads its own from the partner's slot. Lane
-// (g, l16) holds head l16, columns 16cb + 4g + 0..3: one 16-byte store per block. The
-// stores go through a buffer resource spanning the output row; a head past H stores past
-// its end, which the hardware drops, so every wave issues exactly OWN stores.
+// (g, l16) then holds head l16, columns 16cb + 4g + 0..3 of every block. For a pair of
+// blocks (2p, 2p+1) a DPP row rotation trades the halves of the 16-lane rows, so that one
+// store writes whole 128-byte lines (columns 32p .. 32p+31) of heads 0..7 and the next of
+// heads 8..15: lane (g, l16) stores head (l16 & 7) [+ 8], columns 32p + 4(g + 4(l16 >> 3)).
+// The stores go through a buffer resource spanning the output row; a head past H stores
+// past its end, which the hardware drops, so every wave issues exactly OWN stores.
 template <int KH, int CB>
 __device__ __forceinline__ void combine_store(const HalfState &st, const f32x4 (&acc)[CB], float (*meta)[3][16],
                                               f32x4 *xch, int w, int lane, int g, int l16, float *orow, int H,
-                                              int head, int col0, bool bad) {
+                                              int head0, int col0, bool bad) {
     constexpr int OWN = CB / 2;
     constexpr int HALF = OWN / 2;
     const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(orow, 0, H * kHeadDim * 4, kBufferFlags);
@@ -179,7 +187,15 @@ __device__ __forceinline__ void combine_store(const HalfState &st, const f32x4 (
     // x * 1 is x exactly and x * NaN is NaN: a select of constants, so the divide is not
     // put behind a branch and the store count stays the same on every path.
     const float poison = bad ? NAN : 1.0f;
-    const bool hok = head < H;
+    const bool lo_row = l16 < 8;
+    // Output addresses. One block: head head0 + l16, columns col0 + 16cb + 4g. A pair:
+    // heads head0 + (l16 & 7) and + 8, columns col0 + 32p + 4(g + 4(l16 >> 3)).
+    const int h1 = head0 + l16;
+    const int hA = head0 + (l16 & 7), hB = hA + 8;
+    const int base1 = h1 < H ? (h1 * kHeadDim + col0 + 4 * g) * 4 : -1;
+    const int baseA = hA < H ? (hA * kHeadDim + col0 + 4 * (g + 4 * (l16 >> 3))) * 4 : -1;
+    const int baseB = hB < H ? (hB * kHeadDim + col0 + 4 * (g + 4 * (l16 >> 3))) * 4 : -1;
+    auto at = [](int base, int bytes) { return base < 0 ? kDropOffset : base + bytes; };
     float a0 = 0.0f, a1 = 0.0f, lsum = 1.0f;
 #pragma unroll
     for (int r = 0; r < 2; r++) {
@@ -201,18 +217,47 @@ __device__ __forceinline__ void combine_store(const HalfState &st, const f32x4 (
             // contraction the compiler would choose in each instance.
             lsum = __builtin_fmaf(a0, l0, a1 * l1);
         }
-#pragma unroll
-        for (int i = 0; i < HALF; i++) {
-            const int cb = OWN * KH + r * HALF + i;
+        auto finish = [&](int cb, const f32x4 &par) {
             const f32x4 own = acc[cb];
-            const f32x4 par = xch[((w ^ 4) * HALF + i) * 64 + lane];
             const f32x4 x0 = KH ? par : own;
             const f32x4 x1 = KH ? own : par;
             f32x4 o;
 #pragma unroll
             for (int e = 0; e < 4; e++) o[e] = (__builtin_fmaf(a0, x0[e], a1 * x1[e]) / lsum) * poison;
-            const int off = hok ? (head * kHeadDim + col0 + 16 * cb) * 4 : kDropOffset;
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o), rsrc, off, 0, kStoreNT);
+            return o;
+        };
+        // The partner reads go out four at a time ahead of their first use, so their LDS
+        // latency overlaps instead of adding up block by block.
+        constexpr int GRP = HALF < 4 ? HALF : 4;
+#pragma unroll
+        for (int i0 = 0; i0 < HALF; i0 += GRP) {
+            f32x4 parts[GRP];
+#pragma unroll
+            for (int i = 0; i < GRP; i++) parts[i] = xch[((w ^ 4) * HALF + i0 + i) * 64 + lane];
+            if constexpr (GRP >= 2) {
+#pragma unroll
+                for (int i = 0; i < GRP; i += 2) {
+                    const int cb = OWN * KH + r * HALF + i0 + i;  // even
+                    const f32x4 x = finish(cb, parts[i]);
+                    const f32x4 y = finish(cb + 1, parts[i + 1]);
+                    f32x4 sa, sb;
+#pragma unroll
+                    for (int e = 0; e < 4; e++) {
+                        const float xr = ror8(x[e]), yr = ror8(y[e]);
+                        sa[e] = lo_row ? x[e] : yr;
+                        sb[e] = lo_row ? xr : y[e];
+                    }
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, sa), rsrc, at(baseA, 64 * cb), 0,
+                                                           kStoreNT);
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, sb), rsrc, at(baseB, 64 * cb), 0,
+                                                           kStoreNT);
+                }
+            } else {
+                const int cb = OWN * KH + r * HALF + i0;
+                const f32x4 o = finish(cb, parts[0]);
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o), rsrc, at(base1, 64 * cb), 0,
+                                                       kStoreNT);
+            }
         }
     }
 }
@@ -483,11 +528,11 @@ attn_bf16_ks_kernel(AttnArgs a, int n_hg, int64_t units) {
         starting = q_now;
         if (last_of_unit) {
             float *orow = a.out + cur.row * a.H * kHeadDim;
-            const int head = cur.hg * 64 + 16 * hq + l16;
-            const int col0 = cur.cs * COLS + 4 * g;
+            const int head0 = cur.hg * 64 + 16 * hq;
+            const int col0 = cur.cs * COLS;
             f32x4 *xch = (f32x4 *)v_lds;
-            if (kh) combine_store<1>(st, acc, meta_lds, xch, w, lane, g, l16, orow, a.H, head, col0, bad);
-            else combine_store<0>(st, acc, meta_lds, xch, w, lane, g, l16, orow, a.H, head, col0, bad);
+            if (kh) combine_store<1>(st, acc, meta_lds, xch, w, lane, g, l16, orow, a.H, head0, col0, bad);
+            else combine_store<0>(st, acc, meta_lds, xch, w, lane, g, l16, orow, a.H, head0, col0, bad);
             bad = bad_next;
             bad_next = false;
         }
@@ -683,11 +728,11 @@ attn_bf16_ks_alias_kernel(AttnArgs a, int n_hg, int64_t units) {
         starting = q_now;
         if (last_of_unit) {
             float *orow = a.out + cur.row * a.H * kHeadDim;
-            const int head = cur.hg * 64 + 16 * hq + l16;
-            const int col0 = cur.cs * COLS + 4 * g;
+            const int head0 = cur.hg * 64 + 16 * hq;
+            const int col0 = cur.cs * COLS;
             f32x4 *xch = (f32x4 *)(t_lds + buf * kTileBytes);
-            if (kh) combine_store<1>(st, acc, meta_lds, xch, w, lane, g, l16, orow, a.H, head, col0, bad0);
-            else combine_store<0>(st, acc, meta_lds, xch, w, lane, g, l16, orow, a.H, head, col0, bad0);
+            if (kh) combine_store<1>(st, acc, meta_lds, xch, w, lane, g, l16, orow, a.H, head0, col0, bad0);
+            else combine_store<0>(st, acc, meta_lds, xch, w, lane, g, l16, orow, a.H, head0, col0, bad0);
             bad0 = bad1;
             bad1 = bad2;
             bad2 = false;
