@@ -24,8 +24,8 @@ is the decode step above):
   prefill        2,048 query rows at positions 2,048..4,095 over one shared
                  4,096-position cache: causal top-640 (valid_len = pos + 1), then
                  prefill attention at 64 heads
-  prefill-h16    the same with 16 real heads, launched as 16 (the kernel pads to
-                 its 32-head block internally)
+  prefill-h16    the same with 16 real heads, launched as 16 (one 16-head block per
+                 workgroup; its waves split the output columns four ways)
   prefill-pad16  the same 16 heads copied into a zero-padded 32-head buffer with
                  zero sinks, launched at 32 heads, real heads copied out
 """
@@ -61,7 +61,7 @@ def algorithmic_flops(rows: int, heads: int, d: int, k: int) -> int:
 
 
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "attn_decode_b1024_h64_k640_hbm_traffic.md")
-KERNEL_SOURCE = os.path.join(ROOT, "sparse_attention_attn_amd", "csrc", "sa_attn_ks.hip")
+KERNEL_SOURCE = os.path.join(ROOT, "sparse_attention_attn_amd", "csrc", "sa_attn.hip")
 
 
 def measured_traffic(rows: int, heads: int, n_ctx: int, k: int):
@@ -253,8 +253,8 @@ def main() -> int:
             "unit": "GB/s",
             "frac": achieved_gbs / HBM_PEAK_GBS,
             "traffic": None if alias else measured_traffic(B, H, N, K),
-            "kernel": "attn_bf16_ks_alias_kernel<1> (sparse_attn_decode, K = V)" if alias
-                      else "attn_bf16_ks_kernel<1> (sparse_attn_decode)",
+            "kernel": "attn_bf16_alias_kernel<4,1> (sparse_attn_decode, K = V)" if alias
+                      else "attn_bf16_kernel<4,1> (sparse_attn_decode)",
             "kernel_ms": attn_ms,
             "algorithmic_bytes_per_launch": nbytes,
             "mfma_tflops": flops / (attn_ms * 1e-3) / 1e12,
@@ -395,13 +395,13 @@ def bench_prefill(args, torch, sa, w, dev) -> int:
                         f"{N}-position cache, causal indexer top-{K} (valid_len = pos + 1), then sparse "
                         f"attention with per-head sinks at {h_real} real heads"
                         + (" padded to 32 with zero sinks and copied out" if pad else
-                           (" (launched as 16; the kernel pads to its 32-head block)" if h_real == 16 else "")),
+                           (" (launched as 16: one 16-head block per workgroup)" if h_real == 16 else "")),
             "rows": T, "heads": h_real, "launch_heads": h_launch, "head_dim": D, "n_ctx": N, "k": K,
         },
         "roofline": {
             "bound": "mfma", "achieved": tflops, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": tflops / MFMA_BF16_PEAK_TFLOPS, "traffic": None,
-            "kernel": ("attn_bf16_ks_kernel<1>" if h_launch > 32 else "attn_bf16_kernel<1,8>") + " (sparse_attn_prefill)",
+            "kernel": f"attn_bf16_kernel<{4 if h_launch > 32 else (2 if h_launch > 16 else 1)},1> (sparse_attn_prefill)",
             "kernel_ms": attn_ms, "algorithmic_flops_per_launch": flops,
             "gathered_bytes_per_launch": gathered, "gathered_gbs": gathered / (attn_ms * 1e-3) / 1e9,
             "unique_hbm_bytes_per_launch": unique,

@@ -105,8 +105,7 @@ int run_attn(int dtype, const void *q, const void *k, const void *v, int64_t n_c
     a.H = H;
     a.out = out;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const hipError_t e = dtype == SA_BF16 ? (k == v ? sa::launch_attn_bf16_alias(a, s) : sa::launch_attn_bf16(a, s))
-                                          : sa::launch_attn_f32(a, s);
+    const hipError_t e = dtype == SA_BF16 ? sa::launch_attn_bf16(a, s) : sa::launch_attn_f32(a, s);
     if (e != hipSuccess) return fail(SA_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
     return ok();
 }

@@ -1,48 +1,52 @@
-// sa_attn.hip -- gathered sparse attention with per-head sinks, bf16 storage, for gfx950.
+// sa_attn.hip -- gathered sparse attention with per-head sinks, bf16 storage, for gfx950:
+// every tile's keys split between two halves of an eight-wave workgroup. One kernel reads
+// separate K and V caches, the other one cache serving as both (each selected row is then
+// gathered once).
 //
-// What it computes: akol1/TensorFold pull request 4 ("DeepSeek V4.1: sparse
-// attention on eight SIMD groups, the same bytes"), first commit message: for a
-// query row and its heads, the selected keys are scored in 64-key tiles against a
-// 512-wide head (sixteen 32-wide output column groups), with a running maximum, a
-// tile sum and a value sum kept in a fixed order. TensorFold pull request 1206,
-// "What changes": every head has a sink logit (zero for padded heads).
+// What it computes: akol1/TensorFold pull request 4 ("DeepSeek V4.1: sparse attention on
+// eight SIMD groups, the same bytes"), first commit message: for a query row and its heads,
+// the selected keys are scored in 64-key tiles against a 512-wide head (sixteen 32-wide
+// output column groups), with a running maximum, a tile sum and a value sum. TensorFold
+// pull request 1206, "What changes": every head has a sink logit (zero for padded heads).
 //
 // How it maps to CDNA4 (this is not the pages' one-SIMD-group-per-head design):
-//   * One workgroup serves one query row and a block of 32 or 64 heads, because
-//     the key/value latent is shared by all heads of a row: each selected cache
-//     row is gathered from HBM once per row, not once per head.
-//   * The gather is an index-driven direct-to-LDS DMA (global_load_lds_dwordx4):
-//     one wave instruction moves one whole 1 KiB cache row (or the workgroup's
-//     column slice of it), so every gather is a fully coalesced burst. K and V tiles sit in two LDS buffers; the next
-//     tile's K is in flight while the current tile's values are applied, and the
-//     next tile's V while the next scores are formed.
-//   * S^T = K Q^T and O^T = V^T P^T run on v_mfma_f32_32x32x16_bf16 with the heads
-//     on the N side, so every lane owns one head. The two waves of a head block each
-//     hold the query for one half of the head width (64 VGPRs) and form partial
-//     scores for all 64 keys; each hands the other the partials of its key half
-//     through LDS, and both add (half 0 + half 1). The row maximum and the tile sum
-//     are then an in-lane reduction over 16 scores, one exchange with lane^32, and a
-//     fixed-order combine of the two key halves in LDS. V^T operands come from
-//     ds_read_b64_tr_b16 transposing reads.
-//   * Splitting work across workgroups only ever splits heads and output columns,
-//     never keys, so each (row, head, column) is produced by the same sequence of
-//     operations whatever the batch size or head count: results are bit-identical
-//     across launch shapes and repeats, and no workspace or combine pass exists.
+//   * One workgroup serves one query row, a block of 16*HQ heads (HQ = 4, 2 or 1) and
+//     512/NS output columns, on eight waves, two per SIMD, because the key/value latent is
+//     shared by all heads of a row: each selected cache row is gathered from HBM once per
+//     row, not once per head. Wave w takes key half kh = w>>2 of every 64-key tile (keys
+//     32kh .. 32kh+31), and with wi = w&3, heads 16(wi % HQ) .. +15 of the block and column
+//     quarter / half wi / HQ of the slice (one of 4/HQ). Each wave keeps its own online
+//     softmax over its key half; at the end of a unit the two waves that hold the same
+//     heads and columns combine their states through LDS, in a fixed order (half 0, half 1).
+//   * S^T = K Q^T and O^T = V^T P^T run on v_mfma_f32_16x16x32_bf16 with the 16 heads on
+//     the N side. The query (16 heads x 512) stays in 64 registers, so every score is
+//     contracted over the full head width inside one wave.
+//   * K rows sit in the order that makes each lane's four scores of a 16-slot block, for
+//     blocks 0 and 1, exactly the eight weights of its P^T operand (keys 8g .. 8g+7 of
+//     lane group g). So no score, maximum, sum or weight crosses a wave inside a tile: the
+//     row maximum and the tile sum are in-lane reductions plus two lane swaps
+//     (v_permlane16_swap, v_permlane32_swap). The barriers left are those that hand a
+//     gathered buffer from the waves that filled it to the waves that read it, and back.
+//   * Gathers are index-driven direct-to-LDS DMAs through buffer resources (a masked key
+//     reads zeros), issued one row at a time inside the MFMA loops.
+//   * Splitting work across workgroups or waves only ever splits heads and output columns
+//     (each wave's scores are contracted over the whole head width, whatever it stores),
+//     never keys, so results are bit-identical across launch shapes, head counts and
+//     repeats, and the two kernels give the same bits on equal contents.
 //
-// Numerics (the fixed order), in log2 units (x2 = x * log2 e): per 64-key tile,
-// m' = max(m, max_j s_j); the exponent reference r moves to m' (0 if m' = -inf), with
-// alpha = 2^(r - r'), only when m' > r + 8 or r > m' > -inf for one of the wave's 32
-// heads, else alpha = 1; p_j = 2^(s_j - r) rounded to bf16; l = alpha*l + sum_j p_j
-// (the same rounded p); acc = alpha*acc + P V; m = m'. Start: m = sink, r = sink
-// (0 if -inf), l = 2^(sink - r), acc = 0. End: acc / l. The moves of r change only
-// rounding: every p stays below 2^8 and the ratio acc / l is what the definition gives.
-// Keys past a row's count score -inf by select and gather a zero row, so a tail
-// tile never multiplies a stale LDS value.
+// Numerics, in log2 units (x2 = x * log2 e), per wave and 32-key half tile: m' = max(m,
+// max_j s_j); the exponent reference r moves to m' (0 if m' = -inf) with alpha = 2^(r - r')
+// (0 while nothing has been accumulated) when m' > r + 8 or r > m' > -inf for one of the
+// wave's 16 heads, else alpha = 1; p_j = 2^(s_j - r) split into hi + lo, both bf16; l =
+// alpha*l + sum_j (hi + lo); acc = alpha*acc + (hi + lo) V. Half 0 starts from the sink
+// (m = sink, r = sink or 0 if -inf, l = 2^(sink - r)), half 1 from nothing (m = -inf, r = 0,
+// l = 0). End: with R the reference of the half holding the larger maximum and a_h =
+// 2^(r_h - R) (0 for a half with l = 0), out = (a_0 acc_0 + a_1 acc_1) / (a_0 l_0 + a_1 l_1).
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
 
-#include <atomic>
+#include <type_traits>
 
 #include "sa_device.h"
 #include "sa_internal.h"
@@ -50,510 +54,782 @@
 namespace sa {
 namespace {
 
-// Kernel template.
-//   HB: head blocks of 32 per workgroup (1 or 2); the workgroup has 2*HB waves.
-//   NT: 32-column output groups per wave; the workgroup covers 64*NT columns.
-// Wave w: head block hb = w/2; kb = w%2 picks the half of the head width the wave
-// contracts for the scores, the 32-key block of each tile it finishes and
-// normalises, and the half of the workgroup's columns it accumulates.
-template <int HB, int NT>
-__global__ void __launch_bounds__(128 * HB) __attribute__((amdgpu_waves_per_eu(1, 1)))
-attn_bf16_kernel(AttnArgs a, int n_hg, int64_t units) {
-    constexpr int WAVES = 2 * HB;
-    constexpr int COLS = 64 * NT;              // output columns per workgroup
-    constexpr int VROW = COLS * 2;             // bytes of one V row slice
-    constexpr int VSTRIDE = VROW + 64;         // padded V row stride in LDS
-    constexpr int VCHUNKS = VROW / 16;         // 16-byte pieces of a V row slice
-    constexpr int NK = kTile / WAVES;          // K rows gathered per wave per tile
-    constexpr int NV = kTile / WAVES;          // V rows gathered per wave per tile
-    constexpr int N_CS = kHeadDim / COLS;
-    constexpr int kStores = 4 * NT;             // output stores per wave per unit
-    static_assert(NK * WAVES == kTile, "tile split");
-    static_assert(NV + 1 < 64 && NK < 64, "vmcnt range");
+constexpr int kWaves = 8;
+constexpr int kRows = kTile / kWaves;   // rows each wave gathers per tile (per buffer)
 
-    __shared__ __attribute__((aligned(16))) char k_lds[kTile * kKStride];
-    __shared__ __attribute__((aligned(16))) char v_lds[kTile * VSTRIDE];
-    // Per-wave 4 KiB exchange slot: first the partial scores a wave hands its partner,
-    // later in the tile its P operand (the partner has read the partials by then).
-    __shared__ __attribute__((aligned(16))) float xch_lds[WAVES][16][64];
-    __shared__ float max_lds[WAVES][32];
-    __shared__ float sum_lds[WAVES][32];
-    __shared__ int idx_lds[WAVES][2][64];   // each wave's own copy of a tile's index list
+// K slot, within a 32-key half, of key kap = 8g + 4b + r: slot 16b + 4g + r. Row 4g + r of
+// the score MFMA over slots 16b .. 16b+15 lands in lane group g, element r, which is the
+// P^T operand's element 4b + r (key 8g + 4b + r).
+__device__ __forceinline__ int kslot_of_key(int kap) { return ((kap & 4) << 2) | ((kap >> 3) << 2) | (kap & 3); }
 
-    const int lane = threadIdx.x & 63;
-    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int g = lane >> 5;
-    const int ln = lane & 31;
-    const int hb = w >> 1;
-    const int kb = w & 1;
+// LDS row stride of the separate kernel's V buffer: the row bytes plus 32, an odd multiple
+// of 32 for every slice width. A transposing read of the value MFMA's operand touches
+// eight consecutive V slots (V slot of key kap: swap23(kap)) at one 32-byte column
+// window; with an odd multiple of 32 as stride they land on eight different bank windows.
+constexpr int vstride_of(int vrow) { return vrow + 32; }
 
-    // A unit is one (query row, head group, column slice). This workgroup serves units
-    // base, base + G, base + 2G, ... as one stream of 64-key tiles, so the next unit's
-    // first gathers overlap the current unit's last tile. Every unit has at least one
-    // tile (a row with no selected key runs one all-masked tile, which changes nothing).
-    const int64_t G = (int64_t)gridDim.x;
-    const int64_t base = xcd_remap(blockIdx.x, G);
+// Chunk swizzle of the aliased kernel's tile rows (stride 1024): the 16-byte chunk c of
+// the row in slot s is stored at chunk c ^ tswz(s). The score reads (sixteen slots
+// 16b .. 16b+15, one chunk) see sixteen different values of tswz and so sixteen bank
+// groups; the value reads (slots 16t2 + 0..7, or + 8..15, one aligned 32-byte window) see
+// eight different even (or odd) values, which keep each window whole and move the eight
+// windows to eight different places.
+__device__ __forceinline__ int tswz(int s) { return ((s & 7) << 1) | ((s >> 3) & 1); }
 
-    struct Item {          // one tile of one unit (all fields wave-uniform)
-        int64_t unit;      // < 0: none
-        int64_t row;
-        int tile, ntiles, n, hg, cs;
-    };
-    auto make_item = [&](int64_t u) -> Item {
+template <typename T>
+__device__ __forceinline__ const SA_LDS T *lds_at(uint32_t addr) {
+    return (const SA_LDS T *)(uintptr_t)addr;
+}
+
+// Online-softmax state of one wave over its key half, relative to the reference ref.
+struct HalfState {
+    float m, ref, l;
+};
+
+template <int CB>
+__device__ __forceinline__ void half_start(HalfState &st, f32x4 (&acc)[CB], bool with_sink, float sink) {
+    if (with_sink) {
+        const float sink2 = sink * kLog2e;
+        st.m = sink2;
+        st.ref = (sink2 == -INFINITY) ? 0.0f : sink2;
+        st.l = exp2_hw(sink2 - st.ref);
+    } else {
+        st.m = -INFINITY;
+        st.ref = 0.0f;
+        st.l = 0.0f;
+    }
+#pragma unroll
+    for (int cb = 0; cb < CB; cb++) acc[cb] = (f32x4){};
+}
+
+// One half tile. s0, s1: the score MFMA blocks; element 4b + r of this lane is key p0 + 4b
+// + r of the row's list (p0 = 64 tile + 32 kh + 8 g); keys at or past n are masked. Returns
+// the two bf16 parts of the weights as the P^T operand, and updates the state and acc.
+template <int CB>
+__device__ __forceinline__ void half_tile(const f32x4 &s0, const f32x4 &s1, int p0, int n, float scale2,
+                                          HalfState &st, f32x4 (&acc)[CB], bf16x8 &ph, bf16x8 &pl) {
+    float s[8];
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 8; e++) {
+        const float full = e < 4 ? s0[e] : s1[e - 4];
+        s[e] = p0 + e < n ? full * scale2 : -INFINITY;
+        mloc = fmaxf(mloc, s[e]);
+    }
+    mloc = max_xor32(max_xor16(mloc));
+    const float m_new = fmaxf(st.m, mloc);
+    // The reference follows the running maximum lazily: it moves (and l, acc are rescaled
+    // by alpha) only when the maximum has risen more than kLazy above it, or when it sits
+    // above a finite maximum (from the start value 0); the decision is taken for the
+    // wave's 16 heads together. Otherwise alpha = 1 and every p stays <= 2^kLazy.
+    const bool move = m_new > st.ref + kLazy || (m_new < st.ref && m_new != -INFINITY);
+    const bool rescale = __builtin_amdgcn_ballot_w64(move) != 0;
+    float alpha = 1.0f;
+    if (rescale) {
+        const float ref_new = (m_new == -INFINITY) ? 0.0f : m_new;
+        // Nothing accumulated yet (l = 0): the old reference may be arbitrarily far from
+        // the new one, and 0 (not 2^(r - r'), which can overflow) keeps acc at 0.
+        alpha = st.l == 0.0f ? 0.0f : exp2_hw(st.ref - ref_new);
+        st.ref = ref_new;
+    }
+    // p = hi + lo with both parts bf16, so the value product (one MFMA per part) sees p
+    // to about 16 significant bits and l sums the same hi + lo. hi is p truncated toward
+    // zero and lo = bf16(p - hi); when p is itself a positive bf16 value, hi is the next
+    // bf16 below it and lo its last unit, so hi + lo = p exactly, and an infinite value
+    // times a positive weight stays infinite.
+    float psum = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; e++) {
+        const float pf = exp2_hw(s[e] - st.ref);
+        const uint32_t pbits = __float_as_uint(pf);
+        const uint32_t trunc = pbits >> 16;  // a NaN stays a NaN after either step below
+        const bool exact = (pbits & 0xffffu) == 0u && pf > 0.0f;
+        const uint32_t hb = exact ? trunc - 1u : trunc;
+        const float hif = __uint_as_float(hb << 16);
+        const __bf16 hi = __builtin_bit_cast(__bf16, (uint16_t)hb);
+        const __bf16 lo = (__bf16)(pf - hif);
+        psum += hif + (float)lo;
+        ph[e] = hi;
+        pl[e] = lo;
+    }
+    psum = sum_xor32(sum_xor16(psum));
+    st.l = __builtin_fmaf(alpha, st.l, psum);
+    st.m = m_new;
+    if (rescale) [[unlikely]] {
+#pragma unroll
+        for (int cb = 0; cb < CB; cb++) acc[cb] *= alpha;
+    }
+}
+
+// Row rotation by 8 inside each 16-lane row (DPP row_ror:8): lane l16 receives lane l16 ^ 8.
+__device__ __forceinline__ float ror8(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xf, 0xf, false));
+}
+
+// End of a unit: combine the two key halves and store. The pair (w, w ^ 4) holds the same
+// heads; wave kh finalises column blocks OWN*kh .. OWN*kh + OWN-1 in two rounds of OWN/2.
+// Per round each wave writes the partner's blocks (16-byte pieces, lane-major) into its
+// slot of xch (a free gathered buffer) and reads its own from the partner's slot. Lane
+// (g, l16) then holds head l16, columns 16cb + 4g + 0..3 of every block. For a pair of
+// blocks (2p, 2p+1) a DPP row rotation trades the halves of the 16-lane rows, so that one
+// store writes whole 128-byte lines (columns 32p .. 32p+31) of heads 0..7 and the next of
+// heads 8..15: lane (g, l16) stores head (l16 & 7) [+ 8], columns 32p + 4(g + 4(l16 >> 3)).
+// The stores go through a buffer resource spanning the output row; a head past H stores
+// past its end, which the hardware drops, so every wave issues exactly OWN stores.
+template <int KH, int CB>
+__device__ __forceinline__ void combine_store(const HalfState &st, const f32x4 (&acc)[CB], float (*meta)[3][16],
+                                              f32x4 *xch, int w, int lane, int g, int l16, float *orow, int H,
+                                              int head0, int col0, bool bad) {
+    constexpr int OWN = CB / 2;
+    constexpr int HALF = OWN / 2;
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(orow, 0, H * kHeadDim * 4, kBufferFlags);
+    if (g == 0) {
+        meta[w][0][l16] = st.m;
+        meta[w][1][l16] = st.ref;
+        meta[w][2][l16] = st.l;
+    }
+    // x * 1 is x exactly and x * NaN is NaN: a select of constants, so the divide is not
+    // put behind a branch and the store count stays the same on every path.
+    const float poison = bad ? NAN : 1.0f;
+    const bool lo_row = l16 < 8;
+    // Output addresses. One block: head head0 + l16, columns col0 + 16cb + 4g. A pair:
+    // heads head0 + (l16 & 7) and + 8, columns col0 + 32p + 4(g + 4(l16 >> 3)).
+    const int h1 = head0 + l16;
+    const int hA = head0 + (l16 & 7), hB = hA + 8;
+    const int base1 = h1 < H ? (h1 * kHeadDim + col0 + 4 * g) * 4 : -1;
+    const int baseA = hA < H ? (hA * kHeadDim + col0 + 4 * (g + 4 * (l16 >> 3))) * 4 : -1;
+    const int baseB = hB < H ? (hB * kHeadDim + col0 + 4 * (g + 4 * (l16 >> 3))) * 4 : -1;
+    auto at = [](int base, int bytes) { return base < 0 ? kDropOffset : base + bytes; };
+    float a0 = 0.0f, a1 = 0.0f, lsum = 1.0f;
+#pragma unroll
+    for (int r = 0; r < 2; r++) {
+        // Round 0: every wave is past its value products (the buffer is free).
+        // Round 1: every partner has read round 0.
+        lds_barrier();
+#pragma unroll
+        for (int i = 0; i < HALF; i++) xch[(w * HALF + i) * 64 + lane] = acc[OWN * (1 - KH) + r * HALF + i];
+        lds_barrier();
+        if (r == 0) {
+            const int p = w ^ 4;
+            const float mp = meta[p][0][l16], rp = meta[p][1][l16], lp = meta[p][2][l16];
+            const float m0 = KH ? mp : st.m, r0 = KH ? rp : st.ref, l0 = KH ? lp : st.l;
+            const float m1 = KH ? st.m : mp, r1 = KH ? st.ref : rp, l1 = KH ? st.l : lp;
+            const float R = m0 >= m1 ? r0 : r1;
+            a0 = l0 == 0.0f ? 0.0f : exp2_hw(r0 - R);
+            a1 = l1 == 0.0f ? 0.0f : exp2_hw(r1 - R);
+            // Explicit fused forms: the order of the two products is fixed, whatever
+            // contraction the compiler would choose in each instance.
+            lsum = __builtin_fmaf(a0, l0, a1 * l1);
+        }
+        auto finish = [&](int cb, const f32x4 &par) {
+            const f32x4 own = acc[cb];
+            const f32x4 x0 = KH ? par : own;
+            const f32x4 x1 = KH ? own : par;
+            f32x4 o;
+#pragma unroll
+            for (int e = 0; e < 4; e++) o[e] = (__builtin_fmaf(a0, x0[e], a1 * x1[e]) / lsum) * poison;
+            return o;
+        };
+        // The partner reads go out four at a time ahead of their first use, so their LDS
+        // latency overlaps instead of adding up block by block.
+        constexpr int GRP = HALF < 4 ? HALF : 4;
+#pragma unroll
+        for (int i0 = 0; i0 < HALF; i0 += GRP) {
+            f32x4 parts[GRP];
+#pragma unroll
+            for (int i = 0; i < GRP; i++) parts[i] = xch[((w ^ 4) * HALF + i0 + i) * 64 + lane];
+            if constexpr (GRP >= 2) {
+#pragma unroll
+                for (int i = 0; i < GRP; i += 2) {
+                    const int cb = OWN * KH + r * HALF + i0 + i;  // even
+                    const f32x4 x = finish(cb, parts[i]);
+                    const f32x4 y = finish(cb + 1, parts[i + 1]);
+                    f32x4 sa, sb;
+#pragma unroll
+                    for (int e = 0; e < 4; e++) {
+                        const float xr = ror8(x[e]), yr = ror8(y[e]);
+                        sa[e] = lo_row ? x[e] : yr;
+                        sb[e] = lo_row ? xr : y[e];
+                    }
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, sa), rsrc, at(baseA, 64 * cb), 0,
+                                                           kStoreNT);
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, sb), rsrc, at(baseB, 64 * cb), 0,
+                                                           kStoreNT);
+                }
+            } else {
+                const int cb = OWN * KH + r * HALF + i0;
+                const f32x4 o = finish(cb, parts[0]);
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o), rsrc, at(base1, 64 * cb), 0,
+                                                       kStoreNT);
+            }
+        }
+    }
+}
+
+// Work items shared by both kernels. A unit is one (query row, head group of 64, column
+// slice); a workgroup serves units base, base + G, ... as one stream of 64-key tiles (at
+// least one per unit; a row with no selected key runs one all-masked tile, which changes
+// nothing). useq counts the units this workgroup has started, to tell whose bad-index
+// flag a resolved list belongs to.
+struct Item {              // all fields wave-uniform
+    int64_t unit;          // < 0: none
+    int64_t row;
+    int tile, ntiles, n, hg, cs, useq;
+};
+
+template <int NS>
+struct Stream {
+    const AttnArgs &a;
+    int n_hg;
+    int64_t units, G;
+    __device__ Item make(int64_t u, int useq) const {
         Item it{};
         it.unit = u;
+        it.useq = useq;
         if (u < 0 || u >= units) { it.unit = -1; return it; }
-        it.cs = (int)(u % N_CS);
-        it.hg = (int)((u / N_CS) % n_hg);
-        it.row = u / ((int64_t)N_CS * n_hg);
-        // A scalar (constant address space) load: it waits on the LDS/scalar counter,
-        // not on the vector-memory counter that the in-flight gathers hold.
+        it.cs = (int)(u % NS);
+        it.hg = (int)((u / NS) % n_hg);
+        it.row = u / ((int64_t)NS * n_hg);
+        // A scalar (constant address space) load: it waits on the LDS/scalar counter, not
+        // on the vector-memory counter that the in-flight gathers hold.
         int n = a.nsel ? *(const __attribute__((address_space(4))) int32_t *)(a.nsel + it.row) : a.kmax;
         n = n < 0 ? 0 : (n > a.kmax ? a.kmax : n);
         it.n = n;
         it.tile = 0;
         it.ntiles = n > 0 ? (n + kTile - 1) / kTile : 1;
         return it;
-    };
-    auto next_item = [&](const Item &it) -> Item {
+    }
+    __device__ Item next(const Item &it) const {
         if (it.unit < 0) return it;
         if (it.tile + 1 < it.ntiles) { Item nx = it; nx.tile++; return nx; }
-        return make_item(it.unit + G);
-    };
-    auto idx_row = [&](const Item &it) { return a.idx + it.row * a.kmax; };
-    auto kbase_of = [&](const Item &it) { return (const char *)a.k + it.row * a.cache_stride * 2; };
-    auto vbase_of = [&](const Item &it) {
-        return (const char *)a.v + it.row * a.cache_stride * 2 + (int64_t)it.cs * VROW;
-    };
+        return make(it.unit + G, it.useq + 1);
+    }
+};
 
-    // Index list of an item's tile into this wave's slot buf: lane l fetches entry
-    // tile*64 + l (address clamped to the row). Always issued, also when there is no
-    // item (then the current row's list is re-read), so that every wave issues the same
-    // number of vector-memory operations per tile.
-    auto dma_idx = [&](const Item &it, const Item &fallback, int buf) {
-        const Item &src = it.unit >= 0 ? it : fallback;
-        const int p = (it.unit >= 0 ? it.tile : 0) * kTile + lane;
-        const int pc = p < a.kmax ? p : a.kmax - 1;
-        dma4(idx_row(src), (uint32_t)pc * 4u, lds_addr(&idx_lds[w][buf][0]));
-    };
-    // Row to gather for entry tile*64 + l, or -1 (masked or out of range: gather zeros).
-    auto resolve = [&](const Item &it, int buf, bool &bad) -> int {
-        const int iv = idx_lds[w][buf][lane];
-        const int p = it.tile * kTile + lane;
-        const bool live = p < it.n;
-        const bool inr = iv >= 0 && (int64_t)iv < a.n_ctx;
-        if (__builtin_amdgcn_ballot_w64(live && !inr)) bad = true;
-        return (live && inr) ? iv : -1;
-    };
-    // One DMA instruction gathers one cache row (64 lanes x 16 bytes = 1 KiB) into an
-    // LDS slot; lane i moves bytes [16i, 16i + 16) of the row. Wave w gathers keys
-    // NK*w + i. The buffer resource spans the row's cache; a masked key (-1) has a
-    // wrapped-around offset past its end and arrives as zeros.
-    // Row DMAs are issued one at a time, spread through the tile's compute, so that the
-    // CU's address unit (16 cycles per 1 KiB row) never queues a burst of them.
+// Index list of an item's tile into one of this wave's LDS slots: lane l fetches entry
+// tile*64 + l (address clamped to the row). Always issued, also when there is no item (then
+// the fallback's list is re-read), so that every wave issues the same number of
+// vector-memory operations per tile.
+__device__ __forceinline__ void dma_idx(const AttnArgs &a, const Item &it, const Item &fallback, int *slot, int lane) {
+    const Item &src = it.unit >= 0 ? it : fallback;
+    const int p = (it.unit >= 0 ? it.tile : 0) * kTile + lane;
+    const int pc = p < a.kmax ? p : a.kmax - 1;
+    dma4(a.idx + src.row * a.kmax, (uint32_t)pc * 4u, lds_addr(slot));
+}
+// Row to gather for entry tile*64 + l, or -1 (masked or out of range: gather zeros); bad is
+// set when a live entry (inside the row's count) is out of range.
+__device__ __forceinline__ int resolve(const AttnArgs &a, const Item &it, const int *slot, int lane, bool &bad) {
+    const int iv = slot[lane];
+    const int p = it.tile * kTile + lane;
+    const bool live = p < it.n;
+    const bool inr = iv >= 0 && (int64_t)iv < a.n_ctx;
+    bad = __builtin_amdgcn_ballot_w64(live && !inr) != 0;
+    return (live && inr) ? iv : -1;
+}
+
+// The next unit's query and sink, loaded asynchronously into qreg (the previous unit's last
+// scores have been formed by then); usable after a wait that covers them and register_ready.
+// Lane (g, l16) holds head head0 + l16, dims 32kk + 8g + 0..7 for kk < 16. Heads
+// past H read zeros (query and sink) from the static zero row.
+__device__ __forceinline__ void load_q_async(const AttnArgs &a, const Item &it, int head0, int g, int l16,
+                                             bf16x8 (&qreg)[16], float &sink) {
+    const int head = head0 + l16;
+    const bool ok = head < a.H;
+    const uint16_t *qrow =
+        ok ? (const uint16_t *)a.q + (it.row * a.H + head) * kHeadDim : (const uint16_t *)g_zero_row;
+    qrow += 8 * g;
+#pragma unroll
+    for (int kk = 0; kk < 16; kk++) load16_async(qreg[kk], qrow + 32 * kk);
+    load4_async(sink, ok ? a.sinks + head : (const float *)g_zero_row);
+}
+__device__ __forceinline__ void q_ready(bf16x8 (&qreg)[16], float &sink) {
+#pragma unroll
+    for (int kk = 0; kk < 16; kk++) register_ready(qreg[kk]);
+    register_ready(sink);
+}
+
+// ---------------------------------------------------------------------------------------
+// Separate K and V caches. One K buffer and one V buffer of 64 rows each: V(j) is gathered
+// while the scores of tile j run, K(j+1) while its values are applied. Two barriers per
+// tile: "K(j) landed, V buffer free" and "V(j) landed, K buffer free".
+template <int HQ, int NS>
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+attn_bf16_kernel(AttnArgs a, int n_hg, int64_t units) {
+    constexpr int CQ = 4 / HQ;                 // column parts per key half
+    constexpr int COLS = kHeadDim / NS;        // output columns per workgroup
+    constexpr int WCOLS = COLS / CQ;           // output columns per wave
+    constexpr int CB = WCOLS / 16;             // 16-column blocks of the value MFMA per wave
+    constexpr int VROW = COLS * 2;             // bytes of one V row slice
+    constexpr int VSTRIDE = vstride_of(VROW);
+    constexpr int VCHUNKS = VROW / 16;         // 16-byte pieces of a V row slice
+    constexpr int kStores = CB / 2;            // output stores per wave per unit
+    static_assert(kRows == 8 && CB >= 4 && HQ * CQ == 4, "tile split");
+    static_assert(kWaves * (CB / 4) * 1024 <= kTile * VSTRIDE, "the exchange fits the V buffer");
+    static_assert(kStores + kRows < 64, "vmcnt range");
+
+    __shared__ __attribute__((aligned(16))) char k_lds[kTile * kKStride];
+    __shared__ __attribute__((aligned(16))) char v_lds[kTile * VSTRIDE];
+    __shared__ int idx_lds[kWaves][2][64];   // each wave's own copy of a tile's index list
+    __shared__ float meta_lds[kWaves][3][16];
+
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int g = lane >> 4;
+    const int l16 = lane & 15;
+    const int wi = w & 3;
+    const int hq = wi % HQ;
+    const int cq = wi / HQ;
+    const int kh = w >> 2;
+    const Stream<NS> str{a, n_hg, units, (int64_t)gridDim.x};
+
+    // Wave w gathers tile keys 8w .. 8w+7 (all in its own key half) into both buffers: key
+    // 32kh + kap goes to K slot 32kh + kslot_of_key(kap) and to V slot 32kh + swap23(kap).
+    // One DMA instruction moves one cache row (64 lanes x 16 bytes) or its column slice. The
+    // buffer resource spans the row's cache; a masked key (-1) has a wrapped-around offset
+    // past its end and arrives as zeros.
     auto rsrc_k = [&](const Item &it) {
-        return __builtin_amdgcn_make_buffer_rsrc((void *)kbase_of(it), 0, (int)(uint32_t)(a.n_ctx * kRowBytes),
-                                                 kBufferFlags);
+        return __builtin_amdgcn_make_buffer_rsrc((void *)((const char *)a.k + it.row * a.cache_stride * 2), 0,
+                                                 (int)(uint32_t)(a.n_ctx * kRowBytes), kBufferFlags);
     };
     auto rsrc_v = [&](const Item &it) {
         return __builtin_amdgcn_make_buffer_rsrc(
-            (void *)vbase_of(it), 0, (int)(uint32_t)(a.n_ctx * kRowBytes - (int64_t)it.cs * VROW), kBufferFlags);
+            (void *)((const char *)a.v + it.row * a.cache_stride * 2 + (int64_t)it.cs * VROW), 0,
+            (int)(uint32_t)(a.n_ctx * kRowBytes - (int64_t)it.cs * VROW), kBufferFlags);
     };
     auto dma_k_row = [&](__amdgpu_buffer_rsrc_t rsrc, int iv, int i) {
-        const int ij = __builtin_amdgcn_readlane(iv, NK * w + i);
-        dma16_buf(rsrc, ((uint32_t)ij << 10) + ((uint32_t)lane << 4),
-                  lds_addr((SA_LDS char *)k_lds + (NK * w + swap23(i)) * kKStride));
+        const int ij = __builtin_amdgcn_readlane(iv, kRows * w + i);
+        const int slot = 32 * kh + kslot_of_key(8 * wi + i);
+        dma16_buf(rsrc, ((uint32_t)ij << 10) + ((uint32_t)lane << 4), lds_addr((SA_LDS char *)k_lds + slot * kKStride));
     };
-    // V rows keep the tile's key order; only the unit's column slice is moved.
     auto dma_v_row = [&](__amdgpu_buffer_rsrc_t rsrc, int iv, int i) {
-        const int j = w * NV + i;
-        const int ij = __builtin_amdgcn_readlane(iv, j);
+        const int ij = __builtin_amdgcn_readlane(iv, kRows * w + i);
+        const int slot = 32 * kh + swap23(8 * wi + i);
         if (VCHUNKS == 64 || lane < VCHUNKS)
-            dma16_buf(rsrc, ((uint32_t)ij << 10) + ((uint32_t)lane << 4), lds_addr(v_lds + j * VSTRIDE));
+            dma16_buf(rsrc, ((uint32_t)ij << 10) + ((uint32_t)lane << 4), lds_addr((SA_LDS char *)v_lds + slot * VSTRIDE));
     };
 
-    // Per-unit state. Query operand of S^T = K Q^T over this wave's half kb of the head
-    // width: lane (head ln, half g) holds d = 256 kb + 128 g + 8 kk + 0..7, kk < 16.
-    // Softmax state in log2 units: scores and the sink are multiplied by log2(e) so that
-    // exp(x - y) = exp2(x2 - y2) runs on v_exp_f32. m_run is the running maximum, ref the
-    // exponent reference that l_run and acc are relative to (see the tile update).
     const float scale2 = a.scale * kLog2e;
     bf16x8 qreg[16];
-    f32x16 acc[NT];
-    float m_run, ref, l_run;
-    // The next unit's query and sink are loaded asynchronously (load_q_async, then
-    // start_unit once a wait has covered them), so a unit boundary needs no drain. The
-    // query lands in qreg itself: the previous unit's last scores have been formed.
+    f32x4 acc[CB];       // head l16, columns 16cb + 4g + 0..3 of the slice
+    HalfState st;
     float sink_n;
-    int head_n;
-    bool head_ok_n;
-    auto load_q_async = [&](const Item &it) {
-        head_n = (it.hg * HB + hb) * 32 + ln;
-        head_ok_n = head_n < a.H;
-        // Heads past H read zeros (query and sink) from the static zero row.
-        const uint16_t *qrow = head_ok_n ? (const uint16_t *)a.q + (it.row * a.H + head_n) * kHeadDim
-                                         : (const uint16_t *)g_zero_row;
-        qrow += 256 * kb + 128 * g;
-#pragma unroll
-        for (int kk = 0; kk < 16; kk++) load16_async(qreg[kk], qrow + 8 * kk);
-        load4_async(sink_n, head_ok_n ? a.sinks + head_n : (const float *)g_zero_row);
-    };
-    // After a vector-memory wait that covers load_q_async: the loaded registers become
-    // ordinary values (register_ready), and the unit's state starts from its sink.
-    auto start_unit = [&]() {
-#pragma unroll
-        for (int kk = 0; kk < 16; kk++) register_ready(qreg[kk]);
-        register_ready(sink_n);
-        const float sink2 = sink_n * kLog2e;
-        m_run = sink2;
-        ref = (sink2 == -INFINITY) ? 0.0f : sink2;
-        l_run = exp2_hw(sink2 - ref);
-#pragma unroll
-        for (int nt = 0; nt < NT; nt++) acc[nt] = (f32x16){};
-    };
-    // Normalise and store. Lane (g, ln) holds head ln, columns 32nt + 8eq + 4g + 0..3 of
-    // the wave's slice, for eq < 4. Per 32-column group nt the wave's 32 x 32 block goes
-    // through its own 4 KiB exchange slot: written by MFMA lane, read back so that eight
-    // lanes hold one head's 128 contiguous bytes, then stored as whole 128-byte lines.
-    // In the slot, 16-byte chunk c of head row r sits at chunk c ^ ((r >> 1) & 7): both the
-    // writes (sixteen rows, one chunk) and the reads (two rows, eight chunks) of every
-    // sixteen lanes then touch sixteen different bank groups.
-    // The stores go through a buffer resource spanning the unit's output row; a lane
-    // whose head is past H stores past its end, which the hardware drops. So every wave
-    // issues exactly kStores stores, which the vector-memory waits below count on.
-    auto leave_unit = [&](const Item &it, bool bad) {
-        const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-            a.out + it.row * a.H * kHeadDim, 0, a.H * kHeadDim * 4, kBufferFlags);
-        SA_LDS char *slot = (SA_LDS char *)&xch_lds[w][0][0];
-        // x * 1 is x exactly and x * NaN is NaN: a select of constants, so the divide is
-        // not put behind a branch and the store count stays the same on every path.
-        const float poison = bad ? NAN : 1.0f;
-        const int rd_row = lane >> 3, rd_chunk = lane & 7;
-        const int head0 = (it.hg * HB + hb) * 32;
-        const int col0 = it.cs * COLS + kb * NT * 32;
-#pragma unroll
-        for (int nt = 0; nt < NT; nt++) {
-#pragma unroll
-            for (int eq = 0; eq < 4; eq++) {
-                f32x4 o;
-#pragma unroll
-                for (int i = 0; i < 4; i++) o[i] = (acc[nt][4 * eq + i] / l_run) * poison;
-                const int c = 2 * eq + g;
-                *(SA_LDS f32x4 *)(slot + ln * 128 + 16 * (c ^ ((ln >> 1) & 7))) = o;
-            }
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-                const int r = 8 * i + rd_row;
-                const f32x4 o = *(const SA_LDS f32x4 *)(slot + r * 128 + 16 * (rd_chunk ^ ((r >> 1) & 7)));
-                const int h = head0 + r;
-                const int off = h < a.H ? (h * kHeadDim + col0 + 32 * nt + 4 * rd_chunk) * 4 : kDropOffset;
-                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o), rsrc, off, 0, kStoreNT);
-            }
-        }
-    };
 
     // Issue order per wave: Q/sink(0), I(0) | drain | K(0), I(1); then in tile j: V(j)
     // spread through the scores; on a unit's last tile the next unit's query and sink
     // (kQLoads) once V(j) has landed; K(j+1) spread through the values; then I(j+2),
     // followed on a unit's last tile by its kStores output stores. Each wait below counts
     // exactly the operations issued after the one it needs.
-    Item cur = make_item(base);
-    Item nx = next_item(cur);
-    Item nx2 = next_item(nx);
+    Item cur = str.make(xcd_remap(blockIdx.x, str.G), 0);
+    Item nx = str.next(cur);
+    Item nx2 = str.next(nx);
     bool bad = false, bad_next = false;
-    load_q_async(cur);
-    dma_idx(cur, cur, 0);
+    load_q_async(a, cur, cur.hg * 16 * HQ + 16 * hq, g, l16, qreg, sink_n);
+    dma_idx(a, cur, cur, &idx_lds[w][0][0], lane);
     wait_vmcnt<0>();
-    start_unit();
+    q_ready(qreg, sink_n);
+    half_start(st, acc, kh == 0, sink_n);
     __builtin_amdgcn_s_waitcnt(0);  // nothing the compiler tracks is pending in the loop
-    bool starting = false;          // the next unit's query is in flight
-    bool stores_out = false;        // the previous tile ended a unit: its stores follow I(j+1)
-    int iv_cur = resolve(cur, 0, bad);  // rows of the current tile (its V goes out with the scores)
+    bool starting = false;          // the next unit's query is in flight; its stores follow I(j+1)
+    int iv_cur = resolve(a, cur, &idx_lds[w][0][0], lane, bad);
     {
         const __amdgpu_buffer_rsrc_t rk = rsrc_k(cur);
 #pragma unroll
-        for (int i = 0; i < NK; i++) dma_k_row(rk, iv_cur, i);
-        dma_idx(nx, cur, 1);
+        for (int i = 0; i < kRows; i++) dma_k_row(rk, iv_cur, i);
+        dma_idx(a, nx, cur, &idx_lds[w][1][0], lane);
     }
+
+    // Per-lane LDS read bases. Scores: slot 32kh + 16b + l16, dims 32kk + 8g + 0..7.
+    const SA_LDS char *krow = (const SA_LDS char *)k_lds + (32 * kh + l16) * kKStride + 16 * g;
+    // Values: lane (g, l16) addresses the V slot of key 8g + 4t2 + l16/4 of its half and
+    // columns 16cb + 4(l16%4) .. +3 of the wave's part; the transposing read returns column
+    // 16cb + l16 of keys 8g + 4t2 + 0..3, which are elements 4t2 + 0..3 of the V^T operand.
+    const SA_LDS char *vrow = (const SA_LDS char *)v_lds + (32 * kh + swap23(8 * g + (l16 >> 2))) * VSTRIDE +
+                              2 * cq * WCOLS + 8 * (l16 & 3);
 
     for (int j = 0; cur.unit >= 0; j++) {
         const bool more = nx.unit >= 0;
         const bool last_of_unit = !more || nx.unit != cur.unit;
         // K(j) has landed for this wave, and with it a unit's query and sink when tile j
-        // starts one (issued just before K(j)). After K(j) come I(j+1) and, when tile j
-        // starts a unit, the previous unit's stores.
+        // starts one. After K(j) come I(j+1) and, when tile j starts a unit, the previous
+        // unit's stores.
         if (starting) wait_vmcnt<vm_clamp(1 + kStores)>(); else wait_vmcnt<1>();
         if (starting) {
-            start_unit();
-            starting = false;
+            q_ready(qreg, sink_n);
+            half_start(st, acc, kh == 0, sink_n);
         }
-        lds_barrier();
+        lds_barrier();  // every wave's K(j) has landed; every wave is done with V(j-1)
 
-        // ---- partial scores over this wave's half kb of the head width, for both
-        // 32-key blocks of the tile: S^T (keys) x (32 heads); K from LDS, Q in registers.
-        f32x16 sacc0 = (f32x16){}, sacc1 = (f32x16){};
+        // ---- scores of the wave's 32 keys for its 16 heads over the full head width.
+        f32x4 sacc0 = (f32x4){}, sacc1 = (f32x4){};
         {
-            // Software-pipelined: the operands of step kk+1 are read before the two
-            // MFMAs of step kk issue, so LDS latency hides behind the matrix pipe.
-            // The tile's V rows go out here, NV / 16 per step, in the matrix pipe's shadow
-            // (every wave finished the previous tile's values before the barrier above).
             const __amdgpu_buffer_rsrc_t rv = rsrc_v(cur);
-            const SA_LDS char *krow = (const SA_LDS char *)k_lds + ln * kKStride + 512 * kb + 256 * g;
             bf16x8 k0 = *(const SA_LDS bf16x8 *)(krow);
-            bf16x8 k1 = *(const SA_LDS bf16x8 *)(krow + 32 * kKStride);
+            bf16x8 k1 = *(const SA_LDS bf16x8 *)(krow + 16 * kKStride);
 #pragma unroll
             for (int kk = 0; kk < 16; kk++) {
                 bf16x8 n0 = k0, n1 = k1;
                 if (kk + 1 < 16) {
-                    n0 = *(const SA_LDS bf16x8 *)(krow + 16 * (kk + 1));
-                    n1 = *(const SA_LDS bf16x8 *)(krow + 32 * kKStride + 16 * (kk + 1));
+                    n0 = *(const SA_LDS bf16x8 *)(krow + 64 * (kk + 1));
+                    n1 = *(const SA_LDS bf16x8 *)(krow + 16 * kKStride + 64 * (kk + 1));
                 }
-                sacc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qreg[kk], sacc0, 0, 0, 0);
-                sacc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qreg[kk], sacc1, 0, 0, 0);
-#pragma unroll
-                for (int r = 0; r < NV / 16; r++) dma_v_row(rv, iv_cur, kk * (NV / 16) + r);
+                sacc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qreg[kk], sacc0, 0, 0, 0);
+                sacc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qreg[kk], sacc1, 0, 0, 0);
+                // The tile's V rows go out here, one every two steps, in the matrix pipe's
+                // shadow (every wave finished the previous tile's values before the barrier).
+                if (kk % 2 == 0) dma_v_row(rv, iv_cur, kk / 2);
                 __builtin_amdgcn_sched_barrier(0);
                 k0 = n0;
                 k1 = n1;
             }
         }
-        // Hand the partner (the other half of the head width) its key block's partials.
-        {
-            const f32x16 give = kb ? sacc0 : sacc1;
-#pragma unroll
-            for (int c = 0; c < 4; c++)  // chunk c of every lane is contiguous: 16-byte writes
-                ((f32x4 *)&xch_lds[w][0][0])[64 * c + lane] =
-                    (f32x4){give[4 * c], give[4 * c + 1], give[4 * c + 2], give[4 * c + 3]};
-        }
-        lds_barrier();  // partials exchanged; every wave is also done reading k_lds
 
         // Indices of item j+1 have landed (after them: [stores], V(j)).
-        if (stores_out) wait_vmcnt<vm_clamp(kStores + NV)>(); else wait_vmcnt<NV>();
+        if (starting) wait_vmcnt<vm_clamp(kStores + kRows)>(); else wait_vmcnt<kRows>();
+        starting = false;
         int iv_n = 0;
         const bool q_now = last_of_unit && more;
-        if (more) iv_n = resolve(nx, (j + 1) & 1, nx.unit == cur.unit ? bad : bad_next);
-        const __amdgpu_buffer_rsrc_t rk = rsrc_k(nx);
+        if (more) {
+            bool b;
+            iv_n = resolve(a, nx, &idx_lds[w][(j + 1) & 1][0], lane, b);
+            if (nx.unit == cur.unit) bad = bad || b; else bad_next = bad_next || b;
+        }
 
-        // Full scores of key block kb: (half 0 + half 1) of the head width, the same
-        // sum in both waves of the pair. Element e of this lane is key
-        // kb*32 + 16*(e/8) + 8g + e%8 of the tile.
-        const f32x16 own = kb ? sacc1 : sacc0;
-        f32x4 part[4];
-#pragma unroll
-        for (int c = 0; c < 4; c++) part[c] = ((const f32x4 *)&xch_lds[w ^ 1][0][0])[64 * c + lane];
-        float s[16];
-        float mloc = -INFINITY;
-#pragma unroll
-        for (int e = 0; e < 16; e++) {
-            const float full = own[e] + part[e >> 2][e & 3];
-            const int p = cur.tile * kTile + kb * 32 + 16 * (e >> 3) + 8 * g + (e & 7);
-            s[e] = p < cur.n ? full * scale2 : -INFINITY;
-            mloc = fmaxf(mloc, s[e]);
-        }
-        mloc = max_xor32(mloc);
-        if (g == 0) max_lds[w][ln] = mloc;
-        lds_barrier();  // maxima exchanged; every wave is done reading the partials
-
-        // ---- online softmax with the sink, fixed order. The reference follows the
-        // running maximum lazily: it moves (and l_run, acc are rescaled by alpha) only
-        // when the maximum has risen more than kLazy above it, or when it sits above a
-        // finite maximum (only possible from the start value 0 of a -inf sink); the
-        // decision is taken for the wave's 32 heads together. Otherwise alpha = 1 and
-        // the accumulators are left alone; every p stays <= 2^kLazy.
-        const float mt = fmaxf(max_lds[2 * hb][ln], max_lds[2 * hb + 1][ln]);
-        const float m_new = fmaxf(m_run, mt);
-        const bool move = m_new > ref + kLazy || (m_new < ref && m_new != -INFINITY);
-        const bool rescale = __builtin_amdgcn_ballot_w64(move) != 0;
-        float alpha = 1.0f;
-        if (rescale) {
-            const float ref_new = (m_new == -INFINITY) ? 0.0f : m_new;
-            // Nothing accumulated yet (l = 0, from a -inf sink): the old reference may be
-            // arbitrarily far above the new one, and 0 (not 2^(r - r'), which can overflow
-            // to inf and make inf * 0) keeps l and acc at 0.
-            alpha = l_run == 0.0f ? 0.0f : exp2_hw(ref - ref_new);
-            ref = ref_new;
-        }
-        // p = hi + lo with both parts bf16, so the value product (one MFMA per part) sees
-        // p to about 16 significant bits and l sums the same hi + lo. For p > 0 both parts
-        // are positive, so an infinite value times a positive weight stays infinite (never
-        // inf - inf or 0 * inf): hi is p truncated toward zero and lo = bf16(p - hi); when
-        // p is itself a bf16 value, hi is the next bf16 below it and lo its last unit, so
-        // hi + lo = p exactly (exact sums stay exact).
-        bf16x8 ph0, ph1, pl0, pl1;
-        float psum = 0.0f;
-#pragma unroll
-        for (int e = 0; e < 16; e++) {
-            const float pf = exp2_hw(s[e] - ref);
-            const uint32_t pbits = __float_as_uint(pf);
-            const uint32_t trunc = pbits >> 16;  // a NaN stays a NaN after either step below
-            const bool exact = (pbits & 0xffffu) == 0u && pf > 0.0f;
-            const uint32_t hb = exact ? trunc - 1u : trunc;
-            const float hif = __uint_as_float(hb << 16);
-            const __bf16 hi = __builtin_bit_cast(__bf16, (uint16_t)hb);
-            const __bf16 lo = (__bf16)(pf - hif);
-            psum += hif + (float)lo;
-            if (e < 8) { ph0[e] = hi; pl0[e] = lo; } else { ph1[e - 8] = hi; pl1[e - 8] = lo; }
-        }
-        psum = sum_xor32(psum);
-        bf16x8 *p_out = (bf16x8 *)&xch_lds[w][0][0];
-        p_out[lane] = ph0;
-        p_out[64 + lane] = ph1;
-        p_out[128 + lane] = pl0;
-        p_out[192 + lane] = pl1;
-        if (g == 0) sum_lds[w][ln] = psum;
+        bf16x8 ph, pl;
+        half_tile(sacc0, sacc1, cur.tile * kTile + 32 * kh + 8 * g, cur.n, scale2, st, acc, ph, pl);
 
         // V(j) has landed: nothing was issued after it.
         wait_vmcnt<0>();
         // On a unit's last tile: the next unit's query (the scores were qreg's last use),
         // ahead of the K rows, so the wait for K(j+1) covers it too.
-        if (q_now) load_q_async(nx);
-        lds_barrier();
+        if (q_now) load_q_async(a, nx, nx.hg * 16 * HQ + 16 * hq, g, l16, qreg, sink_n);
+        lds_barrier();  // every wave's V(j) has landed; every wave is done with K(j)
 
-        l_run = alpha * l_run + (sum_lds[2 * hb][ln] + sum_lds[2 * hb + 1][ln]);
-        m_run = m_new;
-
-        if (rescale) [[unlikely]] {
+        // ---- values O^T += V^T P^T over the wave's 32 keys, one MFMA per part of P.
+        {
+            const __amdgpu_buffer_rsrc_t rk = rsrc_k(nx);
+            auto read_v = [&](int cb) -> bf16x8 {
+                const bf16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((SA_LDS bf16x4 *)(vrow + 32 * cb));
+                const bf16x4 t1 =
+                    __builtin_amdgcn_ds_read_tr16_b64_v4bf16((SA_LDS bf16x4 *)(vrow + 8 * VSTRIDE + 32 * cb));
+                return (bf16x8){t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3]};
+            };
+            bf16x8 vcur = read_v(0);
 #pragma unroll
-            for (int nt = 0; nt < NT; nt++) {
-                acc[nt] *= alpha;
-                __builtin_amdgcn_sched_barrier(0);  // one 16-register group at a time
-            }
-        }
-
-        // ---- values O^T += V^T P^T over the tile's four 16-key steps.
-        bf16x8 pop[4], pol[4];  // hi and lo parts of P
+            for (int cb = 0; cb < CB; cb++) {
+                bf16x8 vnxt = vcur;
+                if (cb + 1 < CB) vnxt = read_v(cb + 1);
+                acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vcur, ph, acc[cb], 0, 0, 0);
+                acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vcur, pl, acc[cb], 0, 0, 0);
+                // The next tile's K rows go out here, in the matrix pipe's shadow (every
+                // wave is past this tile's scores: the K buffer is free).
+                if (more) {
 #pragma unroll
-        for (int ks = 0; ks < 4; ks++) {
-            const bf16x8 *src = (const bf16x8 *)&xch_lds[2 * hb + (ks >> 1)][0][0];
-            pop[ks] = src[64 * (ks & 1) + lane];
-            pol[ks] = src[128 + 64 * (ks & 1) + lane];
-        }
-        // Lane (g, ch, l16) addresses row 16ks + 8g + 4t2 + l16/4 and columns
-        // 32nt + 16ch + 4(l16%4) .. +3 of the wave's half of the slice; the
-        // transposing read returns column 32nt + 16ch + l16 of rows +0..3.
-        const int l16 = lane & 15;
-        const int ch = (lane >> 4) & 1;
-        const SA_LDS char *vrow = (const SA_LDS char *)v_lds + (8 * g + (l16 >> 2)) * VSTRIDE +
-                                  2 * (kb * NT * 32 + 16 * ch + 4 * (l16 & 3));
-        // Software-pipelined over the column groups: the four V^T operands of group
-        // nt+1 (eight transposing reads) are issued before the four MFMAs of group nt.
-        auto read_v = [&](int nt, bf16x8 (&vop)[4]) {
-#pragma unroll
-            for (int ks = 0; ks < 4; ks++) {
-#pragma unroll
-                for (int t2 = 0; t2 < 2; t2++) {
-                    const bf16x4 part = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                        (SA_LDS bf16x4 *)(vrow + (16 * ks + 4 * t2) * VSTRIDE + 64 * nt));
-                    vop[ks][4 * t2 + 0] = part[0];
-                    vop[ks][4 * t2 + 1] = part[1];
-                    vop[ks][4 * t2 + 2] = part[2];
-                    vop[ks][4 * t2 + 3] = part[3];
+                    for (int r = cb * kRows / CB; r < (cb + 1) * kRows / CB; r++) dma_k_row(rk, iv_n, r);
                 }
+                __builtin_amdgcn_sched_barrier(0);
+                vcur = vnxt;
             }
-        };
-        bf16x8 vcur[4], vnxt[4];
-        read_v(0, vcur);
-#pragma unroll
-        for (int nt = 0; nt < NT; nt++) {
-            if (nt + 1 < NT) read_v(nt + 1, vnxt);
-#pragma unroll
-            for (int ks = 0; ks < 4; ks++) {
-                acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vcur[ks], pop[ks], acc[nt], 0, 0, 0);
-                acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vcur[ks], pol[ks], acc[nt], 0, 0, 0);
-            }
-            // The next tile's K rows go out here, NK / NT per column group, in the matrix
-            // pipe's shadow (every wave is past this tile's scores: the K buffer is free).
-            if (more) {
-#pragma unroll
-                for (int r = 0; r < NK / NT; r++) dma_k_row(rk, iv_n, nt * (NK / NT) + r);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int ks = 0; ks < 4; ks++) vcur[ks] = vnxt[ks];
         }
-        lds_barrier();  // every wave is done with v_lds and the P operands
 
-        dma_idx(nx2, cur, j & 1);  // slot j&1 held item j's list, consumed above
+        dma_idx(a, nx2, cur, &idx_lds[w][j & 1][0], lane);  // slot j&1 held item j's list
         iv_cur = iv_n;
-        stores_out = last_of_unit;
         starting = q_now;
         if (last_of_unit) {
-            leave_unit(cur, bad);
+            float *orow = a.out + cur.row * a.H * kHeadDim;
+            const int head0 = cur.hg * 16 * HQ + 16 * hq;
+            const int col0 = cur.cs * COLS + cq * WCOLS;
+            f32x4 *xch = (f32x4 *)v_lds;
+            if (kh) combine_store<1>(st, acc, meta_lds, xch, w, lane, g, l16, orow, a.H, head0, col0, bad);
+            else combine_store<0>(st, acc, meta_lds, xch, w, lane, g, l16, orow, a.H, head0, col0, bad);
             bad = bad_next;
             bad_next = false;
         }
         cur = nx;
         nx = nx2;
-        nx2 = next_item(nx2);
+        nx2 = str.next(nx2);
     }
     wait_vmcnt<0>();
 }
 
-template <int HB, int NT>
-hipError_t launch_variant(const AttnArgs &a, int64_t units, int64_t grid, hipStream_t s) {
-    const int n_hg = (a.H + 32 * HB - 1) / (32 * HB);
-    hipLaunchKernelGGL((attn_bf16_kernel<HB, NT>), dim3((unsigned)grid), dim3(128 * HB), 0, s, a, n_hg, units);
+// ---------------------------------------------------------------------------------------
+// One cache as K and V. Two tile buffers of 64 full rows alternate: tile j+1 is gathered
+// during all of tile j (half of its rows in the scores, half in the values), and one
+// barrier per tile hands buffers over ("T(j) landed; every wave is done with tile j-1, so
+// its buffer may be refilled"). Index lists run two tiles ahead of the compute. Rows are
+// stored with stride 1024 and the chunk swizzle tswz (applied on the gather side: lane i
+// of a row's DMA fetches chunk i ^ tswz(slot)), and the LDS reads undo it by XOR.
+template <int HQ, int NS>
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+attn_bf16_alias_kernel(AttnArgs a, int n_hg, int64_t units) {
+    constexpr int CQ = 4 / HQ;
+    constexpr int COLS = kHeadDim / NS;
+    constexpr int WCOLS = COLS / CQ;
+    constexpr int CB = WCOLS / 16;
+    constexpr int kStores = CB / 2;
+    constexpr int kTileBytes = kTile * kRowBytes;
+    static_assert(kRows == 8 && CB >= 4 && HQ * CQ == 4, "tile split");
+    static_assert(kWaves * (CB / 4) * 1024 <= kTileBytes, "the exchange fits a tile buffer");
+
+    __shared__ __attribute__((aligned(1024))) char t_lds[2 * kTileBytes];
+    __shared__ int idx_lds[kWaves][2][64];
+    __shared__ float meta_lds[kWaves][3][16];
+
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int g = lane >> 4;
+    const int l16 = lane & 15;
+    const int wi = w & 3;
+    const int hq = wi % HQ;
+    const int cq = wi / HQ;
+    const int kh = w >> 2;
+    const Stream<NS> str{a, n_hg, units, (int64_t)gridDim.x};
+    const uint32_t t_base = lds_addr((SA_LDS char *)t_lds);
+
+    auto rsrc_t = [&](const Item &it) {
+        if (it.unit < 0) return __builtin_amdgcn_make_buffer_rsrc((void *)a.k, 0, 0, kBufferFlags);
+        return __builtin_amdgcn_make_buffer_rsrc((void *)((const char *)a.k + it.row * a.cache_stride * 2), 0,
+                                                 (int)(uint32_t)(a.n_ctx * kRowBytes), kBufferFlags);
+    };
+    // Wave w gathers tile keys 8w .. 8w+7 of its key half into K slots (as the separate
+    // kernel's K buffer), whole rows, swizzled.
+    auto dma_t_row = [&](__amdgpu_buffer_rsrc_t rsrc, int iv, int buf, int i) {
+        const int ij = __builtin_amdgcn_readlane(iv, kRows * w + i);
+        const int slot = 32 * kh + kslot_of_key(8 * wi + i);
+        const uint32_t src_chunk = (uint32_t)(lane ^ tswz(slot));
+        dma16_buf(rsrc, ((uint32_t)ij << 10) + (src_chunk << 4), t_base + buf * kTileBytes + slot * kRowBytes);
+    };
+
+    const float scale2 = a.scale * kLog2e;
+    bf16x8 qreg[16];
+    f32x4 acc[CB];
+    HalfState st;
+    float sink_n;
+
+    // Read bases within a buffer (XOR with the per-step column offset; bits 4-9 only).
+    // Scores: slot 32kh + 16b + l16, chunk 4kk + g, stored at (4kk + g) ^ tswz(l16).
+    const uint32_t kbase = (uint32_t)((32 * kh + l16) * kRowBytes + 16 * (g ^ tswz(l16)));
+    // Values: lane (g, l16) reads the slot of key 8g + 4t2 + l16/4 of its half, which is
+    // K slot 16t2 + 4g + l16/4, columns 16cb + 4(l16%4) .. +3: chunk 2cb + h (h = (l16%4)/2),
+    // stored at (2cb + h) ^ tswz(slot), plus 8 bytes for odd l16.
+    const int vslot = 32 * kh + 4 * g + (l16 >> 2);
+    const uint32_t vbase =
+        (uint32_t)(vslot * kRowBytes + 8 * (l16 & 1) + 16 * (((l16 & 3) >> 1) ^ tswz(vslot)));
+
+    // Issue order per wave: Q/sink(0), I(0), I(1) | drain | T(0), I(2); then in tile j:
+    // half of T(j+1) through the scores, on a unit's last tile the next unit's query and
+    // sink (kQLoads), the rest of T(j+1) through the values, then I(j+3) and on a unit's
+    // last tile its kStores output stores.
+    Item cur = str.make(xcd_remap(blockIdx.x, str.G), 0);
+    Item nx = str.next(cur);
+    Item nx2 = str.next(nx);
+    bool bad0 = false, bad1 = false, bad2 = false;  // units cur.useq, +1, +2
+    int cur_useq = 0;
+    auto note_bad = [&](const Item &it, bool b) {
+        const int d = it.useq - cur_useq;
+        bad0 = bad0 || (b && d == 0);
+        bad1 = bad1 || (b && d == 1);
+        bad2 = bad2 || (b && d == 2);
+    };
+    load_q_async(a, cur, cur.hg * 16 * HQ + 16 * hq, g, l16, qreg, sink_n);
+    dma_idx(a, cur, cur, &idx_lds[w][0][0], lane);
+    dma_idx(a, nx, cur, &idx_lds[w][1][0], lane);
+    wait_vmcnt<0>();
+    q_ready(qreg, sink_n);
+    half_start(st, acc, kh == 0, sink_n);
+    __builtin_amdgcn_s_waitcnt(0);
+    int iv_next = 0;  // rows of the tile after the current one
+    {
+        bool b;
+        const int iv0 = resolve(a, cur, &idx_lds[w][0][0], lane, b);
+        note_bad(cur, b);
+        if (nx.unit >= 0) {
+            iv_next = resolve(a, nx, &idx_lds[w][1][0], lane, b);
+            note_bad(nx, b);
+        }
+        const __amdgpu_buffer_rsrc_t rt = rsrc_t(cur);
+#pragma unroll
+        for (int i = 0; i < kRows; i++) dma_t_row(rt, iv0, 0, i);
+        dma_idx(a, nx2, cur, &idx_lds[w][0][0], lane);
+    }
+    bool starting = false;      // tile j starts a unit whose query was loaded in tile j-1
+    bool stores_prev = false;   // tile j-1 ended a unit: its stores follow I(j+2)
+
+    for (int j = 0; cur.unit >= 0; j++) {
+        const int buf = j & 1;
+        const bool more = nx.unit >= 0;
+        const bool last_of_unit = !more || nx.unit != cur.unit;
+        const bool q_now = last_of_unit && more;
+        // T(j) has landed for this wave (and the query, issued before its last rows).
+        // After T(j) come I(j+2) and, when tile j-1 ended a unit, its stores.
+        if (stores_prev) wait_vmcnt<vm_clamp(1 + kStores)>(); else wait_vmcnt<1>();
+        if (starting) {
+            q_ready(qreg, sink_n);
+            half_start(st, acc, kh == 0, sink_n);
+        }
+        lds_barrier();  // every wave's T(j) has landed; every wave is done with tile j-1
+
+        const uint32_t tb = t_base + buf * kTileBytes;
+        const __amdgpu_buffer_rsrc_t rt = rsrc_t(nx);
+        // ---- scores of the wave's 32 keys for its 16 heads over the full head width.
+        f32x4 sacc0 = (f32x4){}, sacc1 = (f32x4){};
+        {
+            const uint32_t kb = tb + kbase;
+            bf16x8 k0 = *lds_at<bf16x8>(kb);
+            bf16x8 k1 = *lds_at<bf16x8>(kb + 16 * kRowBytes);
+#pragma unroll
+            for (int kk = 0; kk < 16; kk++) {
+                bf16x8 n0 = k0, n1 = k1;
+                if (kk + 1 < 16) {
+                    n0 = *lds_at<bf16x8>(kb ^ (64u * (kk + 1)));
+                    n1 = *lds_at<bf16x8>((kb ^ (64u * (kk + 1))) + 16 * kRowBytes);
+                }
+                sacc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qreg[kk], sacc0, 0, 0, 0);
+                sacc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qreg[kk], sacc1, 0, 0, 0);
+                // Rows 0..3 of T(j+1), one every four steps.
+                if (more && kk % 4 == 0) dma_t_row(rt, iv_next, buf ^ 1, kk / 4);
+                __builtin_amdgcn_sched_barrier(0);
+                k0 = n0;
+                k1 = n1;
+            }
+        }
+        // The scores were the last use of qreg in this unit.
+        if (q_now) load_q_async(a, nx, nx.hg * 16 * HQ + 16 * hq, g, l16, qreg, sink_n);
+
+        bf16x8 ph, pl;
+        half_tile(sacc0, sacc1, cur.tile * kTile + 32 * kh + 8 * g, cur.n, scale2, st, acc, ph, pl);
+
+        // ---- values O^T += V^T P^T over the wave's 32 keys, one MFMA per part of P.
+        {
+            const uint32_t vb = tb + vbase;
+            const uint32_t cbase = (uint32_t)(cur.cs * COLS * 2 + cq * WCOLS * 2);
+            auto read_v = [&](int cb) -> bf16x8 {
+                const uint32_t ad = vb ^ (cbase + 32u * cb);
+                const bf16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((SA_LDS bf16x4 *)lds_at<bf16x4>(ad));
+                const bf16x4 t1 =
+                    __builtin_amdgcn_ds_read_tr16_b64_v4bf16((SA_LDS bf16x4 *)lds_at<bf16x4>(ad + 16 * kRowBytes));
+                return (bf16x8){t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3]};
+            };
+            bf16x8 vcur = read_v(0);
+#pragma unroll
+            for (int cb = 0; cb < CB; cb++) {
+                bf16x8 vnxt = vcur;
+                if (cb + 1 < CB) vnxt = read_v(cb + 1);
+                acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vcur, ph, acc[cb], 0, 0, 0);
+                acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vcur, pl, acc[cb], 0, 0, 0);
+                // Rows 4..7 of T(j+1).
+                if (more) {
+#pragma unroll
+                    for (int r = cb * 4 / CB; r < (cb + 1) * 4 / CB; r++) dma_t_row(rt, iv_next, buf ^ 1, 4 + r);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                vcur = vnxt;
+            }
+        }
+
+        // Indices of item j+2 have landed: after I(j+2) came [stores of tile j-1's unit],
+        // T(j+1) (when there is a tile j+1) and [the next unit's query].
+        if (nx2.unit >= 0) {
+            wait_vmcnt_dyn((stores_prev ? kStores : 0) + (more ? kRows : 0) + (q_now ? kQLoads : 0));
+            bool b;
+            iv_next = resolve(a, nx2, &idx_lds[w][buf][0], lane, b);
+            note_bad(nx2, b);
+        }
+        const Item nx3 = str.next(nx2);
+        dma_idx(a, nx3, cur, &idx_lds[w][buf ^ 1][0], lane);  // slot buf^1 held I(j+1)
+        stores_prev = last_of_unit;
+        starting = q_now;
+        if (last_of_unit) {
+            float *orow = a.out + cur.row * a.H * kHeadDim;
+            const int head0 = cur.hg * 16 * HQ + 16 * hq;
+            const int col0 = cur.cs * COLS + cq * WCOLS;
+            f32x4 *xch = (f32x4 *)(t_lds + buf * kTileBytes);
+            if (kh) combine_store<1>(st, acc, meta_lds, xch, w, lane, g, l16, orow, a.H, head0, col0, bad0);
+            else combine_store<0>(st, acc, meta_lds, xch, w, lane, g, l16, orow, a.H, head0, col0, bad0);
+            bad0 = bad1;
+            bad1 = bad2;
+            bad2 = false;
+            cur_useq++;
+        }
+        cur = nx;
+        nx = nx2;
+        nx2 = nx3;
+    }
+    wait_vmcnt<0>();
+}
+
+template <int HQ, int NS, bool ALIAS>
+hipError_t launch_variant(const AttnArgs &a, int64_t units, hipStream_t s) {
+    const int n_hg = (a.H + 16 * HQ - 1) / (16 * HQ);
+    const int64_t cus = device_cu_count();
+    const dim3 grid((unsigned)(units < cus ? units : cus));
+    if (ALIAS)
+        hipLaunchKernelGGL((attn_bf16_alias_kernel<HQ, NS>), grid, dim3(512), 0, s, a, n_hg, units);
+    else
+        hipLaunchKernelGGL((attn_bf16_kernel<HQ, NS>), grid, dim3(512), 0, s, a, n_hg, units);
     return hipGetLastError();
 }
 
-constexpr int lds_bytes_of(int HB, int NT) {
-    return kTile * kKStride + kTile * (128 * NT + 64) + 2 * HB * 4096 + 2 * 2 * HB * 32 * 4 + 2 * HB * 512;
+template <bool ALIAS>
+hipError_t launch_plan(const AttnArgs &a, const AttnPlan &p, hipStream_t s) {
+    const int ns = kHeadDim / p.cols_per_wg;
+    switch (p.heads_per_wg) {
+        case 64:
+            switch (ns) {
+                case 1: return launch_variant<4, 1, ALIAS>(a, p.units, s);
+                case 2: return launch_variant<4, 2, ALIAS>(a, p.units, s);
+                case 4: return launch_variant<4, 4, ALIAS>(a, p.units, s);
+                case 8: return launch_variant<4, 8, ALIAS>(a, p.units, s);
+            }
+            break;
+        case 32:
+            switch (ns) {
+                case 1: return launch_variant<2, 1, ALIAS>(a, p.units, s);
+                case 2: return launch_variant<2, 2, ALIAS>(a, p.units, s);
+                case 4: return launch_variant<2, 4, ALIAS>(a, p.units, s);
+            }
+            break;
+        case 16:
+            switch (ns) {
+                case 1: return launch_variant<1, 1, ALIAS>(a, p.units, s);
+                case 2: return launch_variant<1, 2, ALIAS>(a, p.units, s);
+            }
+            break;
+    }
+    return hipErrorInvalidValue;
 }
+
+constexpr int kSmallLds = kWaves * 2 * 64 * 4 + kWaves * 3 * 16 * 4;
 
 }  // namespace
 
 AttnPlan plan_attn_bf16(int64_t rows, int H) {
     AttnPlan p{};
-    const int hb = H > 32 ? 2 : 1;
-    p.heads_per_wg = 32 * hb;
+    const int hq = H > 32 ? 4 : (H > 16 ? 2 : 1);
+    p.heads_per_wg = 16 * hq;
     const int64_t n_hg = (H + p.heads_per_wg - 1) / p.heads_per_wg;
     const int64_t rows_hg = rows * n_hg;
-    // One workgroup per CU fits (the K tile alone is 64 KiB of LDS). With fewer
-    // (row, head block) pairs than CUs, column slices add units; every slice gathers
-    // the full K tile but only its own V columns.
-    int nt = 8;
-    if (rows_hg < 64) nt = 1;
-    else if (rows_hg < 128) nt = 2;
-    else if (rows_hg < 256) nt = 4;
-    p.cols_per_wg = 64 * nt;
-    p.units = rows_hg * (kHeadDim / p.cols_per_wg);
-    if (hb == 2) {  // the eight-wave kernel
-        p.threads = 512;
-        p.lds_bytes = attn_bf16_ks_lds_bytes(p.cols_per_wg, false);
-        return p;
-    }
-    p.threads = 128 * hb;
-    p.lds_bytes = lds_bytes_of(hb, nt);
+    // One workgroup per CU fits (the K tile alone is 65 KiB of LDS). With fewer
+    // (row, head block) pairs than CUs, column slices add units; every slice gathers the
+    // full K tile but only its own V columns. A wave keeps at least 64 columns, so blocks
+    // of fewer heads (more column parts per wave pair) allow fewer slices.
+    int ns = 1;
+    if (rows_hg < 64) ns = 8;
+    else if (rows_hg < 128) ns = 4;
+    else if (rows_hg < 256) ns = 2;
+    const int ns_max = 2 * hq;
+    if (ns > ns_max) ns = ns_max;
+    p.cols_per_wg = kHeadDim / ns;
+    p.units = rows_hg * ns;
+    p.threads = 512;
+    p.lds_bytes = kTile * kKStride + kTile * vstride_of(2 * p.cols_per_wg) + kSmallLds;
+    p.lds_bytes_aliased = 2 * kTile * kRowBytes + kSmallLds;
     return p;
 }
-
-namespace {
-// Compute units of the current device (cached per device): the persistent grid size,
-// since one workgroup of this kernel occupies a CU's LDS.
-int cu_count() {
-    static std::atomic<int> cached[64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    int n = cached[dev].load(std::memory_order_relaxed);
-    if (n > 0) return n;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cached[dev].store(n, std::memory_order_relaxed);
-    return n;
-}
-}  // namespace
 
 hipError_t launch_attn_bf16(const AttnArgs &a, hipStream_t s) {
     const AttnPlan p = plan_attn_bf16(a.rows, a.H);
     if (p.units == 0) return hipSuccess;
-    const int64_t grid = p.units < cu_count() ? p.units : cu_count();
-    const int nt = p.cols_per_wg / 64;
-    if (p.heads_per_wg == 64) return launch_attn_bf16_ks(a, p.cols_per_wg, p.units, s);
-    switch (nt) {
-        case 1: return launch_variant<1, 1>(a, p.units, grid, s);
-        case 2: return launch_variant<1, 2>(a, p.units, grid, s);
-        case 4: return launch_variant<1, 4>(a, p.units, grid, s);
-        default: return launch_variant<1, 8>(a, p.units, grid, s);
-    }
+    return a.k == a.v ? launch_plan<true>(a, p, s) : launch_plan<false>(a, p, s);
 }
 
 }  // namespace sa

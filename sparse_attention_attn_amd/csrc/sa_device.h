@@ -1,5 +1,5 @@
-// sa_device.h -- device-side helpers shared by the bf16 attention kernels
-// (sa_attn.hip: separate K and V caches; sa_attn_alias.hip: one cache serving as both).
+// sa_device.h -- device-side helpers of the bf16 attention kernels (sa_attn.hip: separate
+// K and V caches, and one cache serving as both).
 // Not part of the public ABI.
 #pragma once
 
@@ -145,23 +145,16 @@ __device__ __forceinline__ float sum_xor16(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Bits 2 and 3 of m exchanged. Row m of a 32-key MFMA block holds key pi(m), which
-// makes each lane's sixteen scores two runs of eight consecutive keys (the P operand).
+// Bits 2 and 3 of m exchanged (its own inverse). Key kap = 8g + 4t + q of a 32-key half
+// sits in V slot swap23(kap) = 16(g >> 1) + 8t + 4(g & 1) + q, so the eight keys that one
+// transposing read of the value operand takes (g in {0, 1} or {2, 3}, q < 4, fixed t) are
+// eight consecutive slots.
 __device__ __forceinline__ int swap23(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
 
-// LDS row strides. A K row is padded by 16 bytes: the 16 lanes of one ds_read_b128
-// read 16 consecutive slots at the same column and land on 16 different 16-byte
-// bank groups. A V row is padded by 64 bytes: one ds_read_b64_tr_b16 reads rows
-// {0..3} + 8g of a 16-key step at a 64-byte column window, and with a stride of
-// 64 (mod 256) bytes every 4-byte bank is hit exactly twice by its 512 bytes.
-// Either way each read is one base register plus an immediate offset.
+// LDS row stride of the K buffer: padded by 16 bytes, so the 16 lanes of one ds_read_b128,
+// which read 16 consecutive slots at the same column, land on 16 different 16-byte bank
+// groups; each read is one base register plus an immediate offset.
 constexpr int kKStride = kRowBytes + 16;
-
-// K slot s holds tile key (s & 32) | swap23(s & 31), so MFMA row m of key block kb
-// (which must hold key kb*32 + swap23(m)) reads slot kb*32 + m. The map is its own
-// inverse, and for keys n*w + i (n = 16 or 32, i < n) it is n*w + swap23(i): a wave that
-// gathers a run of n keys writes n slots at a wave base plus constant offsets.
-__device__ __forceinline__ int key_of_slot(int s) { return (s & 32) | swap23(s & 31); }
 
 // Map the linear workgroup id so that the workgroups of one query row (its head
 // groups and column slices, which gather the same cache rows) run on one XCD and

@@ -34,16 +34,10 @@ struct TopkArgs {
 };
 
 // Enqueue helpers; they assume validated arguments and return the HIP launch status.
+// launch_attn_bf16 runs the aliased-cache kernel when a.k == a.v (one cache serving as keys
+// and values: each selected row is gathered once).
 hipError_t launch_attn_bf16(const AttnArgs &a, hipStream_t s);
-// The same operation when a.k == a.v (one cache serving as keys and values): each
-// selected row is gathered once.
-hipError_t launch_attn_bf16_alias(const AttnArgs &a, hipStream_t s);
 hipError_t launch_attn_f32(const AttnArgs &a, hipStream_t s);
-// The eight-wave kernels for blocks of 64 heads and cols = 512, 256, 128 or 64 output
-// columns per workgroup (sa_attn_ks.hip; the aliased one when a.k == a.v), and their
-// static LDS size.
-hipError_t launch_attn_bf16_ks(const AttnArgs &a, int cols, int64_t units, hipStream_t s);
-int attn_bf16_ks_lds_bytes(int cols, bool alias);
 hipError_t launch_topk(const TopkArgs &a, hipStream_t s);
 hipError_t launch_pad_heads(int dtype, const void *q, int64_t rows, int h_real, int h_pad,
                             const float *sinks, void *q_pad, float *sinks_pad, hipStream_t s);
@@ -53,12 +47,13 @@ hipError_t launch_unpad_heads(const float *out_pad, int64_t rows, int h_pad, int
 // Launch geometry of the bf16 attention kernel for a given problem (exposed for the
 // host-side tests through sparse_attn_plan in the API layer).
 struct AttnPlan {
-    int heads_per_wg;   // 32 or 64
-    int cols_per_wg;    // 64, 128, 256 or 512
-    int64_t units;      // (row, head group, column slice) work units; the launch runs
-                        // min(units, compute units) persistent workgroups over them
-    int threads;        // per workgroup
-    int lds_bytes;      // static LDS per workgroup
+    int heads_per_wg;       // 16, 32 or 64
+    int cols_per_wg;        // 64, 128, 256 or 512
+    int64_t units;          // (row, head group, column slice) work units; the launch runs
+                            // min(units, compute units) persistent workgroups over them
+    int threads;            // per workgroup
+    int lds_bytes;          // static LDS per workgroup, separate K and V caches
+    int lds_bytes_aliased;  // the same for one cache serving as both
 };
 AttnPlan plan_attn_bf16(int64_t rows, int H);
 
