@@ -53,7 +53,8 @@ def test_tiny_f32_ragged_and_multi_tile():
 
 @pytest.mark.parametrize("heads", [4, 32, 48, 64, 100])
 def test_bf16_head_counts(heads):
-    """Head counts that are not a multiple of the 32-head MFMA block are padded internally."""
+    """Head counts that are not a multiple of the 16-head MFMA block are padded internally (heads past H
+    read a zero query and are not stored)."""
     c = w.decode_bf16(seed=20 + heads, batch=2, heads=heads, n_ctx=1000, k=200)
     check_case(c, label=f"bf16 H={heads} k=200")
 
