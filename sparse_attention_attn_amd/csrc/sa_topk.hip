@@ -11,10 +11,10 @@
 //
 // Two kernels find T:
 //   * topk_regs_kernel (rows of up to 32,768 scores): each lane keeps 16 to 64 keys
-//     in registers; T is built bit by bit, from the top, as the largest value with
-//     at least k keys >= it: a bisection over all keys until few enough share T's
-//     leading bits, then over those few alone. A row takes 1 to 8 waves; several
-//     waves add their counts through LDS.
+//     in registers; T is found by three radix passes from the top (11, 11 and 10
+//     bits), each an LDS histogram of the keys that share the digits found so far
+//     and one scan that locates the digit where the count from the top reaches k.
+//     A row takes 1 to 8 waves.
 //   * topk_radix_kernel (longer rows): four 8-bit radix passes with LDS
 //     histograms, the keys cached in LDS when the row fits (32,768 scores) and
 //     re-read from memory otherwise.
@@ -37,18 +37,6 @@ __device__ __forceinline__ uint32_t order_key(float x) {
     u = u == 0x80000000u ? 0u : u;
     const uint32_t key = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
     return x != x ? 0u : key;
-}
-
-typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
-
-// Per 16-bit half h of h2: 1 if h > c, else 0, for both halves of cx2 equal to c:
-// min(sat(h - c), 1) on packed unsigned 16-bit lanes (v_pk_sub_u16 with clamp, then
-// v_pk_min_u16). Written out because the compiler otherwise turns it into a compare and
-// select per half.
-__device__ __forceinline__ u16x2 ge_pair(uint32_t h2, uint32_t cx2, uint32_t one2) {
-    uint32_t t;
-    asm("v_pk_sub_u16 %0, %1, %2 clamp\n\tv_pk_min_u16 %0, %0, %3" : "=&v"(t) : "v"(h2), "s"(cx2), "s"(one2));
-    return __builtin_bit_cast(u16x2, t);
 }
 
 __device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
@@ -165,42 +153,40 @@ __global__ void __launch_bounds__(kThreads) topk_radix_kernel(TopkArgs a) {
 }
 
 
-// Sum over the wave of a per-lane count: DPP row shifts build each 16-lane row's
+// Inclusive prefix sum over the wave's lanes: DPP row shifts build each 16-lane row's
 // inclusive sum, the two row broadcasts carry rows 0 and 0..1 upward, and lane 63
 // ends with the total.
-__device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
+__device__ __forceinline__ uint32_t wave_scan(uint32_t v) {
     v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, false);  // row_shr:1
     v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, false);  // row_shr:2
     v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, false);  // row_shr:4
     v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, false);  // row_shr:8
     v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false);  // row_bcast:15
     v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false);  // row_bcast:31
-    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+    return v;
 }
 
 // WAVES waves per row, KPL keys per lane: a wave covers 64 * KPL positions.
 //
-// The threshold T (the k-th largest key) is the largest value with at least k keys
-// at or above it. It is found in two phases that keep the bracket lo <= T < hi,
-// hi = lo + 2^b, with c_lo / c_hi the numbers of keys at or above lo / hi:
-//   coarse: bisection over every key, one bit per step from the top, each step a
-//     per-lane count (compare + add) summed over the row; it stops as soon as at
-//     most kCand keys fall inside the bracket;
-//   fine: those keys (sharing T's upper bits) are compacted through LDS, every wave
-//     loads all of them (at most four per lane), and the remaining bits are decided
-//     over them alone, plus the fixed count of keys above the bracket it started from.
-// At the end hi = T + 1, so c_hi keys are > T and c_lo - c_hi equal T; when all ties
-// are taken (the usual case), the selection is simply key >= T.
+// The threshold T (the k-th largest key) is fixed 11, 11 and 10 bits at a time from the
+// top. Pass p counts, in an LDS histogram over its digit, the row's keys whose higher
+// digits equal those already fixed; every thread then owns 2048 / (64 WAVES) consecutive
+// bins, a prefix sum over the threads gives each thread the count of keys in the bins
+// above its own, and the one thread whose bins hold the crossing (fewer than krem keys
+// above a bin, at least krem with it) publishes the digit and the count above it.
+// krem, the number of keys still to take, starts at k and loses that count every pass;
+// at the end krem keys equal to T are taken (the lowest positions first) and k - krem
+// keys are greater than T.
 template <int WAVES, int KPL>
 __global__ void __launch_bounds__(64 * WAVES) topk_regs_kernel(TopkArgs a) {
-    static_assert(KPL % 4 == 0, "keys per lane pair up twice in the packed count");
     constexpr int kWaveSpan = 64 * KPL;
-    constexpr int kCandPerLane = 4;
-    constexpr uint32_t kCand = 64 * kCandPerLane;
+    constexpr int kBins = 2048;
+    constexpr int kBinsPerThread = kBins / (64 * WAVES);
+    static_assert(kBinsPerThread % 4 == 0, "bins are read and cleared 16 bytes at a time");
     __shared__ uint32_t cnt_lds[2][WAVES];
-    __shared__ uint32_t tot_lds[WAVES];
+    __shared__ __attribute__((aligned(16))) uint32_t hist[kBins];
+    __shared__ uint32_t pick_lds[3];
     constexpr int kStage = 4096;
-    __shared__ uint32_t cand_lds[kCand + 64];
     __shared__ int32_t out_lds[kStage + 64];
 
     const int lane = threadIdx.x & 63;
@@ -236,129 +222,85 @@ __global__ void __launch_bounds__(64 * WAVES) topk_regs_kernel(TopkArgs a) {
 #pragma unroll
     for (int r = 0; r < KPL; r++) key[r] = order_key(x[r]) & live(base + 64 * r);
 
-    // Row-wide sum of one per-wave value, in wave order; the slot alternates so that one
-    // barrier per call suffices.
-    auto row_total = [&](uint32_t c, int slot) -> uint32_t {
-        if constexpr (WAVES == 1) {
-            return c;
-        } else {
-            if (lane == 0) cnt_lds[slot][w] = c;
-            __syncthreads();
-            uint32_t t = 0u;
+    // ---- radix passes. hist starts at zero and every thread clears the bins it read.
+    typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+    u32x4v *hv = (u32x4v *)&hist[threadIdx.x * kBinsPerThread];
 #pragma unroll
-            for (int ww = 0; ww < WAVES; ww++) t += cnt_lds[slot][ww];
-            return t;
+    for (int i = 0; i < kBinsPerThread / 4; i++) hv[i] = (u32x4v){0u, 0u, 0u, 0u};
+    uint32_t prefix = 0u, krem = k, t_count = 0u;
+#pragma unroll
+    for (int pass = 0; pass < 3; pass++) {
+        const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+        const uint32_t dmask = pass == 2 ? 0x3ffu : 0x7ffu;
+        const int hi_shift = pass == 0 ? 32 : (pass == 1 ? 21 : 10);
+        __syncthreads();  // the bins are clear; pick_lds of the last pass has been read
+#pragma unroll
+        for (int r = 0; r < KPL; r++) {
+            const bool in = (base + 64 * r < vl) & (pass == 0 || (key[r] >> hi_shift) == prefix);
+            if (in) atomicAdd(&hist[(key[r] >> shift) & dmask], 1u);
         }
-    };
-
-    // ---- coarse phase. Every tested value is >= 1, so the zero keys past the row never
-    // count; NaN keys (also 0) count only towards c_lo = vl at the start.
-    uint32_t lo = 0u, c_lo = (uint32_t)vl, c_hi = 0u;
-    int bit = 32;  // the bracket is [lo, lo + 2^bit)
-    {
-        // While the tested bit is 16 or higher, the candidate's low half is zero, so
-        // key >= cand compares the upper halves only: two keys per register, counted by
-        // min(sat(h - (c - 1)), 1) on packed 16-bit lanes (1 iff h >= c), no lane masks.
-        uint32_t hk[KPL / 2];
+        __syncthreads();
+        uint32_t h[kBinsPerThread];
+        uint32_t mine = 0u;
 #pragma unroll
-        for (int i = 0; i < KPL / 2; i++) hk[i] = (key[2 * i] >> 16) | (key[2 * i + 1] & 0xffff0000u);
-        const uint32_t one2 = 0x00010001u;
-        while (bit > 16 && c_lo - c_hi > kCand) {
-            bit--;
-            const uint32_t cand = lo | (1u << bit);
-            const uint32_t cm1 = (cand >> 16) - 1u;
-            const uint32_t cm1x2 = cm1 | (cm1 << 16);
-            u16x2 acc0 = (u16x2){0, 0}, acc1 = (u16x2){0, 0};  // two chains in flight
+        for (int i = 0; i < kBinsPerThread / 4; i++) {
+            const u32x4v v = hv[i];
+            hv[i] = (u32x4v){0u, 0u, 0u, 0u};
 #pragma unroll
-            for (int i = 0; i < KPL / 2; i += 2) {
-                acc0 += ge_pair(hk[i], cm1x2, one2);
-                acc1 += ge_pair(hk[i + 1], cm1x2, one2);
+            for (int e = 0; e < 4; e++) {
+                h[4 * i + e] = v[e];
+                mine += v[e];
             }
-            const u16x2 acc = acc0 + acc1;
-            uint32_t c = (uint32_t)acc[0] + (uint32_t)acc[1];
-            c = row_total(wave_sum(c), bit & 1);
-            if (c >= k) { lo = cand; c_lo = c; } else { c_hi = c; }
         }
-    }
-    while (bit > 0 && c_lo - c_hi > kCand) {
-        bit--;
-        const uint32_t cand = lo | (1u << bit);
-        uint32_t c = 0u;
-#pragma unroll
-        for (int r = 0; r < KPL; r++) c += key[r] >= cand ? 1u : 0u;
-        c = row_total(wave_sum(c), bit & 1);
-        if (c >= k) { lo = cand; c_lo = c; } else { c_hi = c; }
-    }
-
-    // ---- fine phase over the keys inside the bracket (at most kCand of them).
-    // Per-key predicates are combined with & (not &&) and every LDS write is issued, to a
-    // spare slot per lane when the key is not taken, so these loops have no branches.
-    if (bit > 0) {
-        const uint32_t span_m1 = bit >= 32 ? 0xffffffffu : (1u << bit) - 1u;
-        auto inside = [&](int r) { return (key[r] - lo <= span_m1) & (base + 64 * r < vl); };
-        uint32_t before = 0u;
+        const uint32_t incl = wave_scan(mine);
         if constexpr (WAVES > 1) {
-            uint32_t mine = 0u;
+            if (lane == 63) cnt_lds[pass & 1][w] = incl;
+        }
+        __syncthreads();
+        uint32_t before = 0u, total = incl;
+        if constexpr (WAVES > 1) {
+            total = 0u;
 #pragma unroll
-            for (int r = 0; r < KPL; r++) mine += (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(inside(r)));
-            if (lane == 0) tot_lds[w] = mine;
+            for (int ww = 0; ww < WAVES; ww++) {
+                const uint32_t c = cnt_lds[pass & 1][ww];
+                before += ww < w ? c : 0u;
+                total += c;
+            }
+        } else {
+            total = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+        }
+        uint32_t run = total - (before + incl);  // keys in the bins above this thread's
+#pragma unroll
+        for (int i = kBinsPerThread - 1; i >= 0; i--) {
+            if (run < krem && run + h[i] >= krem) {
+                pick_lds[0] = (uint32_t)(threadIdx.x * kBinsPerThread + i);
+                pick_lds[1] = run;
+                pick_lds[2] = h[i];
+            }
+            run += h[i];
+        }
+        __syncthreads();
+        prefix = (prefix << (pass == 2 ? 10 : 11)) | pick_lds[0];
+        krem -= pick_lds[1];
+        t_count = pick_lds[2];
+        // One key has the digits found so far: it is T (and krem = 1). Its owner publishes
+        // it, which replaces the remaining passes. (Not with 64 keys per lane, where the
+        // extra loop costs more registers than the pass it saves.)
+        if (KPL <= 16 && pass < 2 && t_count == 1u) {
+#pragma unroll
+            for (int r = 0; r < KPL; r++)
+                if ((base + 64 * r < vl) & ((key[r] >> shift) == prefix)) pick_lds[0] = key[r];
             __syncthreads();
-#pragma unroll
-            for (int ww = 0; ww < WAVES; ww++) before += ww < w ? tot_lds[ww] : 0u;
-        }
-#pragma unroll
-        for (int r = 0; r < KPL; r++) {
-            const bool in = inside(r);
-            const uint64_t m = __builtin_amdgcn_ballot_w64(in);
-            const uint32_t j = before + lanes_below(m);
-            // exactly c_lo - c_hi keys are inside; the bound is a guard
-            cand_lds[(in & (j < kCand)) ? j : kCand + lane] = key[r];
-            before += (uint32_t)__builtin_popcountll(m);
-        }
-        __syncthreads();
-        const uint32_t ncand = c_lo - c_hi;
-        uint32_t ck[kCandPerLane];
-#pragma unroll
-        for (int i = 0; i < kCandPerLane; i++) {
-            const uint32_t j = 64u * i + lane;
-            ck[i] = j < ncand ? cand_lds[j] : 0u;
-        }
-        const uint32_t c_above = c_hi;  // keys >= the bracket's upper end at entry
-        while (bit > 0) {
-            bit--;
-            const uint32_t cand = lo | (1u << bit);
-            uint32_t c = c_above;
-#pragma unroll
-            for (int i = 0; i < kCandPerLane; i++)
-                c += (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(ck[i] >= cand));
-            if (c >= k) { lo = cand; c_lo = c; } else { c_hi = c; }
+            prefix = pick_lds[0];
+            break;
         }
     }
-    const uint32_t T = lo;
-    const uint32_t need = k - c_hi;           // keys equal to T to take, lowest positions first
-    const bool all_ties = need == c_lo - c_hi;
+    const uint32_t T = prefix;
+    const uint32_t need = krem;               // keys equal to T to take, lowest positions first
+    const bool all_ties = need == t_count;
 
-    // ---- ordered selection. Selected before this wave: every key > T there, and its
-    // share of the first `need` ties.
-    uint32_t sel_base = 0u, eq_base = 0u;
-    if constexpr (WAVES > 1) {
-        __syncthreads();  // every wave has read the last coarse totals from cnt_lds
-        uint32_t gt_w = 0u, eq_w = 0u;
-#pragma unroll
-        for (int r = 0; r < KPL; r++) {
-            gt_w += (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(key[r] > T));
-            eq_w += (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64((key[r] == T) & (base + 64 * r < vl)));
-        }
-        if (lane == 0) { cnt_lds[0][w] = gt_w; cnt_lds[1][w] = eq_w; }
-        __syncthreads();
-        uint32_t gt_before = 0u;
-#pragma unroll
-        for (int ww = 0; ww < WAVES; ww++) {
-            gt_before += ww < w ? cnt_lds[0][ww] : 0u;
-            eq_base += ww < w ? cnt_lds[1][ww] : 0u;
-        }
-        sel_base = gt_before + (eq_base < need ? eq_base : need);
-    }
+    // ---- ordered selection. Every wave has read the last pass's totals from cnt_lds
+    // before the barrier that ended that pass, so cnt_lds is free again.
     // Selected positions go to out_lds[pos] (a spare slot per lane otherwise) when the
     // output row fits there, and leave in coalesced stores; else straight to memory.
     const bool staged = k <= (uint32_t)kStage;
@@ -370,15 +312,55 @@ __global__ void __launch_bounds__(64 * WAVES) topk_regs_kernel(TopkArgs a) {
         }
     };
     if (all_ties) {
+        // The usual case: every key >= T is taken; selected before this wave = the
+        // selected keys of the waves before it. With up to 16 keys per lane the ballots are
+        // kept (in scalar registers) for the emit loop, else formed again there.
+        constexpr bool kKeep = KPL <= 16;
+        auto ballot_sel = [&](int r) { return __builtin_amdgcn_ballot_w64((key[r] >= T) & (base + 64 * r < vl)); };
+        uint64_t msel[kKeep ? KPL : 1];
+        uint32_t cnt = 0u;
 #pragma unroll
         for (int r = 0; r < KPL; r++) {
-            const int p = base + 64 * r;
-            const bool sel = (key[r] >= T) & (p < vl);
-            const uint64_t msel = __builtin_amdgcn_ballot_w64(sel);
-            emit(sel, sel_base + lanes_below(msel), p);
-            sel_base += (uint32_t)__builtin_popcountll(msel);
+            const uint64_t m = ballot_sel(r);
+            if constexpr (kKeep) msel[r] = m;
+            cnt += (uint32_t)__builtin_popcountll(m);
+        }
+        uint32_t sel_base = 0u;
+        if constexpr (WAVES > 1) {
+            if (lane == 0) cnt_lds[0][w] = cnt;
+            __syncthreads();
+#pragma unroll
+            for (int ww = 0; ww < WAVES; ww++) sel_base += ww < w ? cnt_lds[0][ww] : 0u;
+        }
+#pragma unroll
+        for (int r = 0; r < KPL; r++) {
+            uint64_t m;
+            if constexpr (kKeep) m = msel[r]; else m = ballot_sel(r);
+            emit(((m >> lane) & 1u) != 0u, sel_base + lanes_below(m), base + 64 * r);
+            sel_base += (uint32_t)__builtin_popcountll(m);
         }
     } else {
+        // Selected before this wave: every key > T there, and its share of the first
+        // `need` ties.
+        uint32_t sel_base = 0u, eq_base = 0u;
+        if constexpr (WAVES > 1) {
+            uint32_t gt_w = 0u, eq_w = 0u;
+#pragma unroll
+            for (int r = 0; r < KPL; r++) {
+                gt_w += (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(key[r] > T));
+                eq_w += (uint32_t)__builtin_popcountll(
+                    __builtin_amdgcn_ballot_w64((key[r] == T) & (base + 64 * r < vl)));
+            }
+            if (lane == 0) { cnt_lds[0][w] = gt_w; cnt_lds[1][w] = eq_w; }
+            __syncthreads();
+            uint32_t gt_before = 0u;
+#pragma unroll
+            for (int ww = 0; ww < WAVES; ww++) {
+                gt_before += ww < w ? cnt_lds[0][ww] : 0u;
+                eq_base += ww < w ? cnt_lds[1][ww] : 0u;
+            }
+            sel_base = gt_before + (eq_base < need ? eq_base : need);
+        }
 #pragma unroll
         for (int r = 0; r < KPL; r++) {
             const int p = base + 64 * r;
@@ -404,12 +386,12 @@ hipError_t launch_topk(const TopkArgs &a, hipStream_t s) {
     if (a.rows == 0) return hipSuccess;
     const dim3 grid((unsigned)a.rows);
     if (a.n <= 64 * 64) {
-        // One wave per row has the most rows in flight; with at most four rows per CU,
-        // four waves per row shorten each row's chain of dependent steps instead.
+        // With at most four rows per CU, eight waves per row shorten each row's chain;
+        // beyond that, four waves per row keep more rows in flight.
         if (a.rows <= 4 * (int64_t)device_cu_count())
-            hipLaunchKernelGGL((topk_regs_kernel<4, 16>), grid, dim3(256), 0, s, a);
+            hipLaunchKernelGGL((topk_regs_kernel<8, 8>), grid, dim3(512), 0, s, a);
         else
-            hipLaunchKernelGGL((topk_regs_kernel<1, 64>), grid, dim3(64), 0, s, a);
+            hipLaunchKernelGGL((topk_regs_kernel<4, 16>), grid, dim3(256), 0, s, a);
     } else if (a.n <= 4 * 64 * 64) {
         hipLaunchKernelGGL((topk_regs_kernel<4, 64>), grid, dim3(256), 0, s, a);
     } else if (a.n <= 8 * 64 * 64) {
