@@ -230,19 +230,23 @@ def test_determinism_and_guards():
         assert torch.equal(o.view(torch.int32), outs[0].view(torch.int32))
 
 
-def test_batch_invariance_across_launch_shapes():
-    """A row's bits do not depend on how many rows share the launch (different launch shapes
-    split heads and columns differently, never keys)."""
+@pytest.mark.parametrize("heads,alias", [(64, False), (32, False), (16, False), (64, True), (16, True)])
+def test_batch_invariance_across_launch_shapes(heads, alias):
+    """A row's bits do not depend on how many rows share the launch: B = 300, 200, 100, 8 and 1
+    select different column slice counts (1, 2, 4 and 8 at 64 heads; at most 4 at 32 heads and
+    2 at 16), which split heads and columns differently, never keys."""
     import sparse_attention_attn_amd as sa
-    from sparse_attention_attn_amd import _lib
-    c = w.decode_bf16(seed=61, batch=300, heads=64, n_ctx=1024, k=640)
+    c = w.decode_bf16(seed=61 + heads, batch=300, heads=heads, n_ctx=1024, k=640)
     d = to_device(c, DEV)
-    say("batch invariance B in {300, 200, 100, 8, 1}")
-    full = sa.decode(d["q"], d["k"], d["v"], d["idx"], d["sinks"], c.scale, d["nsel"])
+    vv = d["k"] if alias else d["v"]
+    say(f"batch invariance H={heads}{' aliased' if alias else ''}, B in {{300, 200, 100, 8, 1}}")
+    full = sa.decode(d["q"], d["k"], vv, d["idx"], d["sinks"], c.scale, d["nsel"])
     for b in (200, 100, 8, 1):
-        part = sa.decode(d["q"][:b], d["k"][:b], d["v"][:b], d["idx"][:b], d["sinks"], c.scale, d["nsel"][:b])
+        part = sa.decode(d["q"][:b], d["k"][:b], vv[:b], d["idx"][:b], d["sinks"], c.scale, d["nsel"][:b])
         torch.cuda.synchronize()
         assert torch.equal(part.view(torch.int32), full[:b].view(torch.int32)), f"B={b}"
+    if alias:
+        c.v = c.k
     ref = run_oracle(c, rows=[0, 150, 299])
     assert_parity(full.cpu().numpy()[[0, 150, 299]], ref[[0, 150, 299]], *BF16_TOL, "B=300 rows")
 
