@@ -61,7 +61,9 @@ def algorithmic_flops(rows: int, heads: int, d: int, k: int) -> int:
 
 
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "attn_decode_b1024_h64_k640_hbm_traffic.md")
-KERNEL_SOURCE = os.path.join(ROOT, "sparse_attention_attn_amd", "csrc", "sa_attn.hip")
+# The attention kernel's sources: the recorded counters apply while their sha256 (of the
+# files' bytes in this order) is unchanged.
+KERNEL_SOURCES = [os.path.join(ROOT, "sparse_attention_attn_amd", "csrc", f) for f in ("sa_attn.hip", "sa_device.h")]
 
 
 def measured_traffic(rows: int, heads: int, n_ctx: int, k: int):
@@ -76,7 +78,7 @@ def measured_traffic(rows: int, heads: int, n_ctx: int, k: int):
         if ":" in line and not line.startswith(("|", " ", "#")):
             key, val = line.split(":", 1)
             fields[key.strip()] = val.strip()
-    sha = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+    sha = hashlib.sha256(b"".join(open(f, "rb").read() for f in KERNEL_SOURCES)).hexdigest()
     if fields.get("kernel_source_sha256") != sha or "traffic_bytes_per_launch" not in fields:
         return None
     return int(fields["traffic_bytes_per_launch"])

@@ -84,23 +84,22 @@ __device__ __forceinline__ uint32_t lds_addr(const SA_LDS void *p) { return (uin
 
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-// Direct-to-LDS gather: lane i moves 16 bytes from sbase + voff_i to LDS address
-// lds + 16 i (M0 holds the wave's LDS base). sbase and lds are wave-uniform. The load is
-// non-temporal: a gathered cache row is used once per query row, and keeping the stream
-// out of the caches' retained set measured 8% faster at 1,024 rows.
-__device__ __forceinline__ void dma16(const void *sbase, uint32_t voff, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 nt"
-                 ::"s"(lds), "v"(voff), "s"(sbase) : "memory", "m0");
-}
-// The same gather through a buffer resource: lane i moves the 16 bytes at byte offset
-// voff_i of the resource to LDS address lds + 16 i. An offset past the resource's range
-// (a masked row's wrapped-around offset) reads as zeros, so masked rows need no
-// separate source and every lane's access stays inside the resource.
+// The gathers below set M0 (the LDS base of a direct-to-LDS load) themselves and name it as
+// clobbered. The compiler reserves M0 and may still warn about the clobber; it emits no M0
+// use of its own in these kernels (every M0 write in the generated code is one of these).
+//
+// Direct-to-LDS gather through a buffer resource: lane i moves the 16 bytes at byte offset
+// voff_i of the resource to LDS address lds + 16 i; lds is wave-uniform. An offset past the
+// resource's range (a masked row's wrapped-around offset) reads as zeros, so masked rows need
+// no separate source and every lane's access stays inside the resource. The load is
+// non-temporal: a gathered cache row is used once per query row, and keeping the stream out
+// of the caches' retained set measured 8% faster at 1,024 rows.
 __device__ __forceinline__ void dma16_buf(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t lds) {
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds"
                  ::"s"(lds), "v"(voff), "s"(rsrc) : "memory", "m0");
 }
-// Same with 4 bytes per lane (LDS address lds + 4 i).
+// Direct-to-LDS load of 4 bytes per lane, from sbase + voff_i to LDS address lds + 4 i (a
+// tile's index list).
 __device__ __forceinline__ void dma4(const void *sbase, uint32_t voff, uint32_t lds) {
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
                  ::"s"(lds), "v"(voff), "s"(sbase) : "memory", "m0");
