@@ -14,6 +14,7 @@ LIB_PATH = os.path.join(HERE, "libsparse_attn.so")
 SA_OK, SA_ERR_NULL, SA_ERR_SHAPE, SA_ERR_UNSUPPORTED, SA_ERR_WORKSPACE, SA_ERR_HIP = range(6)
 SA_F32, SA_BF16 = 0, 1
 SA_OP_DECODE, SA_OP_PREFILL, SA_OP_TOPK = 0, 1, 2
+SA_HEAD_DIM, SA_MAX_HEADS, SA_BF16_MAX_CTX = 512, 128, 4194303
 
 _c = ctypes
 _P = _c.c_void_p

@@ -24,6 +24,13 @@ def test_header_and_binding_agree():
     assert declared_symbols() == sorted(L.SIGNATURES)
 
 
+def test_header_constants_match_binding():
+    text = open(HEADER).read()
+    for name in ("SA_HEAD_DIM", "SA_MAX_HEADS", "SA_BF16_MAX_CTX"):
+        m = re.search(r"#define\s+%s\s+(\d+)" % name, text)
+        assert m and int(m.group(1)) == getattr(L, name), name
+
+
 def test_every_declared_symbol_is_exported():
     lib = L.load()
     for name in declared_symbols():

@@ -210,6 +210,48 @@ def test_sink_minus_inf_scores_far_below_zero(heads, alias):
     assert np.all(np.isfinite(got))
 
 
+@pytest.mark.parametrize("alias", [False, True])
+def test_largest_cache(alias):
+    """Caches of 2^22 - 1 positions, the largest a bf16 cache may hold (4 GiB per sequence and
+    tensor). Rows 0 and 1 select positions at both ends of the range (0, 1, 2^21, 2^22 - 3,
+    2^22 - 2 and random others), so the gathers' 32-bit byte offsets and the buffer range are
+    exercised at their limit. Row 2 also selects 2^22 - 1, one past the last position, inside its
+    count: its output must be all NaN. The oracle evaluates the same selections on a compact
+    copy that holds only the selected rows (nothing else in the caches is read)."""
+    import sparse_attention_attn_amd as sa
+    from sparse_attention_attn_amd import _lib
+    N = _lib.SA_BF16_MAX_CTX
+    rng = np.random.default_rng(96)
+    small = w.decode_bf16(seed=96, batch=3, heads=64, n_ctx=640, k=640, name="largest cache")
+    assert np.array_equal(small.idx, np.tile(np.arange(640, dtype=np.int32), (3, 1)))
+    if alias:
+        small.v = small.k
+    fixed = np.array([0, 1, 1 << 21, N - 2, N - 1], dtype=np.int64)
+    big_idx = np.empty((3, 640), dtype=np.int64)
+    for r in range(3):
+        others = rng.choice(np.arange(2, N - 2, dtype=np.int64), size=640 - len(fixed), replace=False)
+        big_idx[r] = np.sort(np.concatenate([fixed, others]))
+    big_idx[2, -1] = N  # one past the last position (the list stays sorted)
+    say(f"largest cache N={N}{' aliased' if alias else ''}: 3 rows x 640, 64 heads")
+    kd = torch.zeros((3, N, w.D), dtype=torch.bfloat16, device=DEV)
+    vd = kd if alias else torch.zeros((3, N, w.D), dtype=torch.bfloat16, device=DEV)
+    d = to_device(small, DEV)
+    for r in range(3):
+        pos = torch.from_numpy(big_idx[r][big_idx[r] < N]).to(DEV)
+        kd[r, pos] = d["k"][r, : len(pos)]
+        if not alias:
+            vd[r, pos] = d["v"][r, : len(pos)]
+    idx = torch.from_numpy(big_idx.astype(np.int32)).to(DEV)
+    got = sa.decode(d["q"], kd, vd, idx, d["sinks"], small.scale).cpu().numpy()
+    torch.cuda.synchronize()
+    del kd, vd
+    torch.cuda.empty_cache()
+    ref = run_oracle(small, rows=[0, 1])
+    st = assert_parity(got[:2], ref[:2], *BF16_TOL, "largest cache")
+    assert np.isnan(got[2]).all()
+    say(f"  ok {st}")
+
+
 def test_determinism_and_guards():
     """Five repeats are byte-identical and never write outside their output."""
     import sparse_attention_attn_amd as sa
