@@ -51,7 +51,7 @@ def test_tiny_f32_ragged_and_multi_tile():
     check_case(c, label="f32 3 heads k=150 (3 tiles, ragged)")
 
 
-@pytest.mark.parametrize("heads", [4, 32, 48, 64, 100])
+@pytest.mark.parametrize("heads", [1, 4, 16, 32, 48, 64, 100, 128])
 def test_bf16_head_counts(heads):
     """Head counts that are not a multiple of the 16-head MFMA block are padded internally (heads past H
     read a zero query and are not stored)."""
