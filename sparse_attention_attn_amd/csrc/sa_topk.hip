@@ -10,11 +10,11 @@
 // count is an integer, so the result is the unique exact answer.
 //
 // Two kernels find T:
-//   * topk_regs_kernel (rows of up to 32,768 scores): each lane keeps 16 to 64 keys
+//   * topk_regs_kernel (rows of up to 32,768 scores): each lane keeps 8 to 64 keys
 //     in registers; T is found by three radix passes from the top (11, 11 and 10
 //     bits), each an LDS histogram of the keys that share the digits found so far
 //     and one scan that locates the digit where the count from the top reaches k.
-//     A row takes 1 to 8 waves.
+//     A row takes 4 or 8 waves.
 //   * topk_radix_kernel (longer rows): four 8-bit radix passes with LDS
 //     histograms, the keys cached in LDS when the row fits (32,768 scores) and
 //     re-read from memory otherwise.
