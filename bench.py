@@ -129,8 +129,10 @@ def cpu_baseline(inp, scores, out_gpu, idx_gpu, heads, k, budget_s: float, max_r
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    # The part reaches its steady clocks only after tens of milliseconds of this load: with 5
+    # warm-up steps the timed steps ran 5 % slower than after 200 (about 54 ms of work).
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--batch", type=int, default=1024, help="independent sequences per step")
     ap.add_argument("--heads", type=int, default=64)
     ap.add_argument("--n-ctx", type=int, default=4096)
