@@ -107,6 +107,8 @@ __device__ __forceinline__ void dma4(const void *sbase, uint32_t voff, uint32_t 
 // Asynchronous loads into registers: the destination is written when the data
 // returns, which the compiler does not model, so the value may be used only after an
 // explicit vector-memory wait that covers the load, followed by register_ready on it.
+// The compiler must also not copy or spill the destination before that wait (under
+// register pressure it can); tests/test_isa_async_loads.py checks the built code for it.
 __device__ __forceinline__ void load16_async(bf16x8 &dst, const void *p) {
     asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(dst) : "v"(p) : "memory");
 }
