@@ -352,6 +352,10 @@ __device__ __forceinline__ void q_ready(bf16x8 (&qreg)[16], float &sink) {
 // Separate K and V caches. One K buffer and one V buffer of 64 rows each: V(j) is gathered
 // while the scores of tile j run, K(j+1) while its values are applied. Two barriers per
 // tile: "K(j) landed, V buffer free" and "V(j) landed, K buffer free".
+// When every row reads one shared cache (prefill), tile j+1's rows are also prefetched into
+// L2 as soon as its index list is resolved (mid tile j), so that their gathers mostly hit
+// L2: 6-10% shorter at 2,048 rows. With a cache per row (decode) the gathers already run at
+// the HBM rate, and the extra L2 traffic measured 7-22% slower, so there is no prefetch.
 template <int HQ, int NS>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_bf16_kernel(AttnArgs a, int n_hg, int64_t units) {
@@ -371,6 +375,7 @@ attn_bf16_kernel(AttnArgs a, int n_hg, int64_t units) {
     __shared__ __attribute__((aligned(16))) char v_lds[kTile * VSTRIDE];
     __shared__ int idx_lds[kWaves][2][64];   // each wave's own copy of a tile's index list
     __shared__ float meta_lds[kWaves][3][16];
+    __shared__ uint32_t pf_lds[kWaves][64];  // where the L2 prefetches land (never read)
 
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -408,6 +413,11 @@ attn_bf16_kernel(AttnArgs a, int n_hg, int64_t units) {
             dma16_buf(rsrc, ((uint32_t)ij << 10) + ((uint32_t)lane << 4), lds_addr((SA_LDS char *)v_lds + slot * VSTRIDE));
     };
 
+    const bool shared_cache = a.cache_stride == 0;
+    // Prefetch lanes: lane l takes tile key 8w + l/8 (the rows this wave gathers) and its
+    // 128-byte line l%8; V lines past the slice get an offset past the range (nothing).
+    const uint32_t pf_line = (uint32_t)(lane & 7) << 7;
+    const bool pf_v_line = (int)pf_line < VROW;
     const float scale2 = a.scale * kLog2e;
     bf16x8 qreg[16];
     f32x4 acc[CB];       // head l16, columns 16cb + 4g + 0..3 of the slice
@@ -492,13 +502,19 @@ attn_bf16_kernel(AttnArgs a, int n_hg, int64_t units) {
             bool b;
             iv_n = resolve(a, nx, &idx_lds[w][(j + 1) & 1][0], lane, b);
             if (nx.unit == cur.unit) bad = bad || b; else bad_next = bad_next || b;
+            if (shared_cache) {
+                const int ij = __builtin_amdgcn_ds_bpermute((kRows * w + (lane >> 3)) << 2, iv_n);
+                const uint32_t off = ((uint32_t)ij << 10) + pf_line;
+                prefetch4_buf(rsrc_k(nx), off, lds_addr(&pf_lds[w][0]));
+                prefetch4_buf(rsrc_v(nx), pf_v_line ? off : 0xffffff80u, lds_addr(&pf_lds[w][0]));
+            }
         }
 
         bf16x8 ph, pl;
         half_tile(sacc0, sacc1, cur.tile * kTile + 32 * kh + 8 * g, cur.n, scale2, st, acc, ph, pl);
 
-        // V(j) has landed: nothing was issued after it.
-        wait_vmcnt<0>();
+        // V(j) has landed: after it come only the two prefetches, when issued.
+        if (shared_cache && more) wait_vmcnt<2>(); else wait_vmcnt<0>();
         // On a unit's last tile: the next unit's query (the scores were qreg's last use),
         // ahead of the K rows, so the wait for K(j+1) covers it too.
         if (q_now) load_q_async(a, nx, nx.hg * 16 * HQ + 16 * hq, g, l16, qreg, sink_n);
@@ -821,7 +837,7 @@ AttnPlan plan_attn_bf16(int64_t rows, int H) {
     p.cols_per_wg = kHeadDim / ns;
     p.units = rows_hg * ns;
     p.threads = 512;
-    p.lds_bytes = kTile * kKStride + kTile * vstride_of(2 * p.cols_per_wg) + kSmallLds;
+    p.lds_bytes = kTile * kKStride + kTile * vstride_of(2 * p.cols_per_wg) + kSmallLds + kWaves * 64 * 4;
     p.lds_bytes_aliased = 2 * kTile * kRowBytes + kSmallLds;
     return p;
 }

@@ -98,6 +98,13 @@ __device__ __forceinline__ void dma16_buf(__amdgpu_buffer_rsrc_t rsrc, uint32_t 
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds"
                  ::"s"(lds), "v"(voff), "s"(rsrc) : "memory", "m0");
 }
+// L2 prefetch: lane i loads the 4 bytes at byte offset voff_i of the resource with the default
+// cache policy (so the line stays in L2 for a later gather) into LDS address lds + 4 i, a
+// per-wave slot that nothing reads. An offset past the resource's range fetches nothing.
+__device__ __forceinline__ void prefetch4_buf(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+                 ::"s"(lds), "v"(voff), "s"(rsrc) : "memory", "m0");
+}
 // Direct-to-LDS load of 4 bytes per lane, from sbase + voff_i to LDS address lds + 4 i (a
 // tile's index list).
 __device__ __forceinline__ void dma4(const void *sbase, uint32_t voff, uint32_t lds) {
