@@ -317,6 +317,39 @@ def test_aliased_kv_and_prefill_equals_decode():
     assert_parity(pre.cpu().numpy(), run_oracle(c), *BF16_TOL, "aliased")
 
 
+@pytest.mark.parametrize("rows,heads", [(300, 64), (40, 64), (100, 32), (20, 16)])
+def test_shared_cache_prefill_equals_decode_on_copies(rows, heads):
+    """Prefill over one shared cache (whose kernel prefetches each next tile's rows into L2)
+    equals decode over per-row copies of that cache (no prefetch) bit for bit, including
+    NaN rows: ragged counts and masked tails, -1 and out-of-range indices inside a row's
+    count (NaN row) and beyond it (ignored), over launch shapes with one to eight column
+    slices (V rows prefetched whole or in part)."""
+    import sparse_attention_attn_amd as sa
+    n_ctx, k = 1000, 200
+    c = w.prefill_bf16(seed=64 + rows + heads, rows=rows, first_pos=n_ctx - rows, heads=heads, n_ctx=n_ctx, k=k)
+    rng = np.random.default_rng(rows * heads)
+    c.nsel[:] = rng.integers(0, k + 1, size=rows)
+    c.nsel[:4] = [k, 1, 0, 65]
+    c.idx[1, 0] = -1                  # inside the count: NaN row
+    c.idx[3, 64] = n_ctx + 5          # inside the count (65): NaN row
+    c.idx[0, k - 1] = 2 ** 30         # inside the count (k): NaN row
+    c.idx[5, c.nsel[5]:] = n_ctx * 7  # beyond the count: ignored
+    c.idx[6, c.nsel[6]:] = -1
+    d = to_device(c, DEV)
+    say(f"shared-cache prefill vs decode on copies rows={rows} heads={heads}")
+    pre = sa.prefill(d["q"], d["k"], d["v"], d["idx"], d["sinks"], c.scale, d["nsel"])
+    kk = d["k"].unsqueeze(0).expand(rows, -1, -1).contiguous()
+    vv = d["v"].unsqueeze(0).expand(rows, -1, -1).contiguous()
+    dec = sa.decode(d["q"], kk, vv, d["idx"], d["sinks"], c.scale, d["nsel"])
+    torch.cuda.synchronize()
+    assert torch.equal(pre.view(torch.int32), dec.view(torch.int32))
+    got = pre.cpu().numpy()
+    assert np.all(np.isnan(got[[0, 1, 3]])) and np.all(np.isfinite(got[[2, 5, 6]]))
+    sample = [2, 4, 5, 6, rows // 2, rows - 1]
+    st = assert_parity(got[sample], run_oracle(c, rows=sample)[sample], *BF16_TOL, "shared-cache prefill")
+    say(f"  ok {st}")
+
+
 def test_indexer_then_decode_nonfinite():
     """Indexer + attention: exact top-640 of 8 x 32,768 scores feeds decode on caches where
     about 1% of K and V rows carry +inf/-inf/NaN; classes and values follow the oracle."""
