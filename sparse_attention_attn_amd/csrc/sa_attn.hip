@@ -103,18 +103,27 @@ __device__ __forceinline__ void half_start(HalfState &st, f32x4 (&acc)[CB], bool
 }
 
 // One half tile. s0, s1: the score MFMA blocks; element 4b + r of this lane is key p0 + 4b
-// + r of the row's list (p0 = 64 tile + 32 kh + 8 g); keys at or past n are masked. Returns
-// the two bf16 parts of the weights as the P^T operand, and updates the state and acc.
+// + r of the row's list (p0 = 64 tile + 32 kh + 8 g); keys at or past n are masked (whole:
+// the tile lies inside the row's count, so nothing is). Returns the two bf16 parts of the
+// weights as the P^T operand, and updates the state and acc.
 template <int CB>
-__device__ __forceinline__ void half_tile(const f32x4 &s0, const f32x4 &s1, int p0, int n, float scale2,
+__device__ __forceinline__ void half_tile(const f32x4 &s0, const f32x4 &s1, int p0, int n, bool whole, float scale2,
                                           HalfState &st, f32x4 (&acc)[CB], bf16x8 &ph, bf16x8 &pl) {
     float s[8];
     float mloc = -INFINITY;
+    if (whole) {
 #pragma unroll
-    for (int e = 0; e < 8; e++) {
-        const float full = e < 4 ? s0[e] : s1[e - 4];
-        s[e] = p0 + e < n ? full * scale2 : -INFINITY;
-        mloc = fmaxf(mloc, s[e]);
+        for (int e = 0; e < 8; e++) {
+            s[e] = (e < 4 ? s0[e] : s1[e - 4]) * scale2;
+            mloc = fmaxf(mloc, s[e]);
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; e++) {
+            const float full = e < 4 ? s0[e] : s1[e - 4];
+            s[e] = p0 + e < n ? full * scale2 : -INFINITY;
+            mloc = fmaxf(mloc, s[e]);
+        }
     }
     mloc = max_xor32(max_xor16(mloc));
     const float m_new = fmaxf(st.m, mloc);
@@ -136,17 +145,16 @@ __device__ __forceinline__ void half_tile(const f32x4 &s0, const f32x4 &s1, int 
     // to about 16 significant bits and l sums the same hi + lo. hi is p truncated toward
     // zero and lo = bf16(p - hi); when p is itself a positive bf16 value, hi is the next
     // bf16 below it and lo its last unit, so hi + lo = p exactly, and an infinite value
-    // times a positive weight stays infinite.
+    // times a positive weight stays infinite. For p >= 0 both cases are the top half of
+    // bits(p) - 1, saturated at 0 (p = 0 gives hi = lo = 0; a NaN stays a NaN).
     float psum = 0.0f;
 #pragma unroll
     for (int e = 0; e < 8; e++) {
         const float pf = exp2_hw(s[e] - st.ref);
         const uint32_t pbits = __float_as_uint(pf);
-        const uint32_t trunc = pbits >> 16;  // a NaN stays a NaN after either step below
-        const bool exact = (pbits & 0xffffu) == 0u && pf > 0.0f;
-        const uint32_t hb = exact ? trunc - 1u : trunc;
-        const float hif = __uint_as_float(hb << 16);
-        const __bf16 hi = __builtin_bit_cast(__bf16, (uint16_t)hb);
+        const uint32_t hb = __builtin_elementwise_sub_sat(pbits, 1u);
+        const float hif = __uint_as_float(hb & 0xffff0000u);
+        const __bf16 hi = __builtin_bit_cast(__bf16, (uint16_t)(hb >> 16));
         const __bf16 lo = (__bf16)(pf - hif);
         psum += hif + (float)lo;
         ph[e] = hi;
@@ -511,7 +519,8 @@ attn_bf16_kernel(AttnArgs a, int n_hg, int64_t units) {
         }
 
         bf16x8 ph, pl;
-        half_tile(sacc0, sacc1, cur.tile * kTile + 32 * kh + 8 * g, cur.n, scale2, st, acc, ph, pl);
+        half_tile(sacc0, sacc1, cur.tile * kTile + 32 * kh + 8 * g, cur.n, (cur.tile + 1) * kTile <= cur.n, scale2,
+                  st, acc, ph, pl);
 
         // V(j) has landed: after it come only the two prefetches, when issued.
         if (shared_cache && more) wait_vmcnt<2>(); else wait_vmcnt<0>();
@@ -712,7 +721,8 @@ attn_bf16_alias_kernel(AttnArgs a, int n_hg, int64_t units) {
         if (q_now) load_q_async(a, nx, nx.hg * 16 * HQ + 16 * hq, g, l16, qreg, sink_n);
 
         bf16x8 ph, pl;
-        half_tile(sacc0, sacc1, cur.tile * kTile + 32 * kh + 8 * g, cur.n, scale2, st, acc, ph, pl);
+        half_tile(sacc0, sacc1, cur.tile * kTile + 32 * kh + 8 * g, cur.n, (cur.tile + 1) * kTile <= cur.n, scale2,
+                  st, acc, ph, pl);
 
         // ---- values O^T += V^T P^T over the wave's 32 keys, one MFMA per part of P.
         {
