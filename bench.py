@@ -150,8 +150,8 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on exactly one GPU: the path has no multi-GPU mode in this build "
-              "(sharding over rows or heads is described in DESIGN.md); use --gpus 1.", file=sys.stderr)
+        print("bench.py runs on exactly one GPU: the path has no multi-GPU mode (rows and heads would "
+              "shard without communication, one process per GPU); use --gpus 1.", file=sys.stderr)
         return 2
 
     import torch
