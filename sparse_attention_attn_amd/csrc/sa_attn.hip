@@ -362,7 +362,7 @@ __device__ __forceinline__ void q_ready(bf16x8 (&qreg)[16], float &sink) {
 // tile: "K(j) landed, V buffer free" and "V(j) landed, K buffer free".
 // When every row reads one shared cache (prefill), tile j+1's rows are also prefetched into
 // L2 as soon as its index list is resolved (mid tile j), so that their gathers mostly hit
-// L2: 6-10% shorter at 2,048 rows. With a cache per row (decode) the gathers already run at
+// L2: 11-18% shorter at 2,048 rows. With a cache per row (decode) the gathers already run at
 // the HBM rate, and the extra L2 traffic measured 7-22% slower, so there is no prefetch.
 template <int HQ, int NS>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -433,7 +433,8 @@ attn_bf16_kernel(AttnArgs a, int n_hg, int64_t units) {
     float sink_n;
 
     // Issue order per wave: Q/sink(0), I(0) | drain | K(0), I(1); then in tile j: V(j)
-    // spread through the scores; on a unit's last tile the next unit's query and sink
+    // spread through the scores; with a shared cache, once I(j+1) is resolved, the two L2
+    // prefetches of tile j+1; on a unit's last tile the next unit's query and sink
     // (kQLoads) once V(j) has landed; K(j+1) spread through the values; then I(j+2),
     // followed on a unit's last tile by its kStores output stores. Each wait below counts
     // exactly the operations issued after the one it needs.
