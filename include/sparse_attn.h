@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define SA_ABI_VERSION 1
+#define SA_ABI_VERSION 2
 
 /* Status codes. */
 #define SA_OK 0
@@ -71,6 +71,9 @@ extern "C" {
 #define SA_HEAD_DIM 512
 /* Largest number of heads one call accepts. */
 #define SA_MAX_HEADS 128
+/* Largest kmax (index-list length) one attention call accepts: the kernels address a row's
+   list and its 64-key tiles with 32-bit offsets. */
+#define SA_MAX_KMAX (1 << 24)
 /* Largest n_ctx (cache positions) of a bf16 call: 4 GiB of cache per 1 KiB position row.
    Larger bf16 caches are refused with SA_ERR_UNSUPPORTED. */
 #define SA_BF16_MAX_CTX 4194303
@@ -85,9 +88,22 @@ const char *sparse_attn_status_string(int status);
 const char *sparse_attn_last_error(void);
 
 /*
- * Bytes of device workspace an operation needs for the given sizes. The
- * current kernels need none (every reduction stays inside one workgroup), so
- * this returns 0; callers may pass ws = NULL, ws_bytes = 0.
+ * Bytes of device workspace an attention call (op SA_OP_DECODE or SA_OP_PREFILL)
+ * with these sizes needs; 0 for SA_OP_TOPK and for invalid sizes. Pass a buffer
+ * of at least this size, 16-byte aligned, as ws / ws_bytes (NULL / 0 when it is
+ * 0). The workspace is scratch for the call's kernels only: its contents before
+ * and after a call mean nothing, and two calls in flight at once on different
+ * streams need different workspaces.
+ *
+ * Small batches (fewer than 64 rows per block of 64 heads, index lists of at most
+ * 1,024 entries) split the keys of every row across workgroups: each 64-key tile
+ * is scored in its own workgroup and the raw scores go through the workspace
+ * (rows x ceil(kmax / 64) x ceil(heads / 16) x 4 KiB), before the softmax and value
+ * products fold them in key order. Larger batches need no workspace. A row's
+ * result is the same, bit for bit, on either path (the ds4 commit log for
+ * ds4_tp.c: a split that follows the launch must not change the output bytes).
+ * The value depends only on (op, rows, heads, kmax); the float32 path needs none,
+ * so this is an upper bound for it.
  */
 size_t sparse_attn_workspace_bytes(int op, int64_t rows, int32_t heads, int32_t head_dim,
                                    int32_t kmax, int64_t n_ctx);
@@ -104,7 +120,9 @@ size_t sparse_attn_workspace_bytes(int op, int64_t rows, int32_t heads, int32_t 
  *   sinks     [H] float32 per-head sink logits
  *   scale     multiplies q.k (not the sinks)
  *   out       [B, H, D] float32
- * Requires D == 512, 1 <= H <= 128, B >= 0, kmax >= 1, n_ctx >= 1
+ *   ws        device workspace of ws_bytes >= sparse_attn_workspace_bytes(SA_OP_DECODE, B, H,
+ *             D, kmax, n_ctx) bytes (SA_ERR_WORKSPACE if smaller); NULL when that is 0
+ * Requires D == 512, 1 <= H <= 128, B >= 0, 1 <= kmax <= SA_MAX_KMAX, n_ctx >= 1
  * (n_ctx <= SA_BF16_MAX_CTX for SA_BF16).
  */
 int sparse_attn_decode(int dtype, const void *q, const void *k_cache, const void *v_cache,
@@ -120,6 +138,7 @@ int sparse_attn_decode(int dtype, const void *q, const void *k_cache, const void
  *   k_cache   [n_ctx, D], v_cache [n_ctx, D]
  *   idx       [T, kmax], nsel [T] or NULL; a causal caller keeps row t's indices <= its position
  *   out       [T, H, D] float32
+ *   ws        as for decode, sized by sparse_attn_workspace_bytes(SA_OP_PREFILL, T, ...)
  * Each row's result equals what decode returns for that row with the shared
  * cache as its own (the same kernel runs both).
  */

@@ -37,7 +37,8 @@
  *   position ascending; keep the first min(k, valid_len[r]); write those
  *   positions ascending, pad the rest of the row with -1, store the count.
  *
- * Parity pins live in tests/test_oracle_pins.py and tests/test_oracle_topk.py.
+ * Parity pins live in tests/oracle_pins.py (run by tests/test_oracle_pins.py);
+ * tests/test_oracle_mutants.py checks that planted mistakes fail them.
  */
 #include <math.h>
 #include <stdint.h>

@@ -37,6 +37,16 @@ def _need(cond: bool, msg: str) -> None:
         raise ValueError(msg)
 
 
+def _on_device(ref: torch.Tensor, ref_name: str, **tensors) -> None:
+    """Every given tensor (None allowed) lives on ref's device, and that device is a HIP
+    device: a host tensor's pointer must never reach a kernel as a device pointer."""
+    for name, t in tensors.items():
+        if t is not None:
+            _need(isinstance(t, torch.Tensor), f"{name} must be a torch.Tensor")
+            _need(t.device == ref.device, f"{name} is on {t.device}, {ref_name} on {ref.device}")
+    _need(ref.is_cuda, f"{ref_name} must be on a HIP device, not {ref.device}")
+
+
 def _dtype_code(t: torch.Tensor) -> int:
     if t.dtype == torch.bfloat16:
         return SA_BF16
@@ -45,12 +55,11 @@ def _dtype_code(t: torch.Tensor) -> int:
     raise ValueError(f"q/k/v must be bfloat16 or float32, got {t.dtype}")
 
 
-def _attn(shared: bool, q, k_cache, v_cache, idx, sinks, scale, nsel, out):
-    lib = load()
+def _attn(shared: bool, q, k_cache, v_cache, idx, sinks, scale, nsel, out, ws):
+    _need(q.dim() == 3, "q must be [rows, H, D]")
     rows, H, D = q.shape
-    _need(q.is_cuda, "tensors must be on a HIP device")
-    for name, t in (("k_cache", k_cache), ("v_cache", v_cache), ("idx", idx), ("sinks", sinks)):
-        _need(t.device == q.device, f"{name} is on {t.device}, q on {q.device}")
+    _on_device(q, "q", k_cache=k_cache, v_cache=v_cache, idx=idx, sinks=sinks, nsel=nsel, out=out, ws=ws)
+    lib = load()
     code = _dtype_code(q)
     _need(k_cache.dtype == q.dtype and v_cache.dtype == q.dtype, "q, k_cache and v_cache must share a dtype")
     if shared:
@@ -66,52 +75,66 @@ def _attn(shared: bool, q, k_cache, v_cache, idx, sinks, scale, nsel, out):
     for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("idx", idx), ("sinks", sinks)):
         _need(t.is_contiguous(), f"{name} must be contiguous")
     if nsel is not None:
-        _need(nsel.dtype == torch.int32 and nsel.shape == (rows,) and nsel.is_contiguous()
-              and nsel.device == q.device, "nsel must be contiguous int32 [rows] on q's device")
+        _need(nsel.dtype == torch.int32 and nsel.shape == (rows,) and nsel.is_contiguous(),
+              "nsel must be contiguous int32 [rows]")
     if out is None:
         out = torch.empty((rows, H, D), dtype=torch.float32, device=q.device)
     _need(out.dtype == torch.float32 and out.shape == (rows, H, D) and out.is_contiguous(),
           "out must be contiguous float32 [rows, H, D]")
+    kmax = idx.shape[1]
+    need = 0
+    if code == SA_BF16 and 1 <= kmax <= _lib.SA_MAX_KMAX:
+        need = int(lib.sparse_attn_workspace_bytes(_lib.SA_OP_PREFILL if shared else _lib.SA_OP_DECODE,
+                                                   rows, H, D, kmax, n_ctx))
+    if ws is None and need > 0:
+        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if ws is not None:
+        _need(ws.dtype == torch.uint8 and ws.dim() == 1 and ws.is_contiguous(), "ws must be contiguous uint8 [bytes]")
     fn = lib.sparse_attn_prefill if shared else lib.sparse_attn_decode
-    rc = fn(code, _ptr(q), _ptr(k_cache), _ptr(v_cache), n_ctx, _ptr(idx), _ptr(nsel), idx.shape[1],
-            _ptr(sinks), float(scale), rows, H, D, _ptr(out), None, 0, _stream(q))
+    rc = fn(code, _ptr(q), _ptr(k_cache), _ptr(v_cache), n_ctx, _ptr(idx), _ptr(nsel), kmax,
+            _ptr(sinks), float(scale), rows, H, D, _ptr(out), _ptr(ws), 0 if ws is None else ws.numel(), _stream(q))
     _lib.check(rc, fn.__name__, lib)
     return out
 
 
 def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, idx: torch.Tensor,
            sinks: torch.Tensor, scale: float, nsel: Optional[torch.Tensor] = None,
-           out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """sparse_attn_decode: B sequences, each with its own cache. Returns float32 [B, H, 512]."""
-    return _attn(False, q, k_cache, v_cache, idx, sinks, scale, nsel, out)
+           out: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """sparse_attn_decode: B sequences, each with its own cache. Returns float32 [B, H, 512].
+
+    ws: optional uint8 device workspace of at least workspace_bytes(SA_OP_DECODE, ...) bytes;
+    allocated here when needed and not given."""
+    return _attn(False, q, k_cache, v_cache, idx, sinks, scale, nsel, out, ws)
 
 
 def prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, idx: torch.Tensor,
             sinks: torch.Tensor, scale: float, nsel: Optional[torch.Tensor] = None,
-            out: Optional[torch.Tensor] = None) -> torch.Tensor:
+            out: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None) -> torch.Tensor:
     """sparse_attn_prefill: T rows over one shared cache [N, 512]. Returns float32 [T, H, 512]."""
-    return _attn(True, q, k_cache, v_cache, idx, sinks, scale, nsel, out)
+    return _attn(True, q, k_cache, v_cache, idx, sinks, scale, nsel, out, ws)
 
 
 def topk(scores: torch.Tensor, k: int, valid_len: Optional[torch.Tensor] = None,
          idx_out: Optional[torch.Tensor] = None,
          count_out: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """sparse_attn_topk: exact top-k per row. Returns (idx int32 [R, k], count int32 [R])."""
+    _on_device(scores, "scores", valid_len=valid_len, idx_out=idx_out, count_out=count_out)
     lib = load()
-    _need(scores.is_cuda and scores.dtype == torch.float32 and scores.dim() == 2,
-          "scores must be float32 [rows, n] on a HIP device")
+    _need(scores.dtype == torch.float32 and scores.dim() == 2, "scores must be float32 [rows, n]")
     _need(scores.stride(1) == 1, "scores rows must be contiguous")
     rows, n = scores.shape
     ld = scores.stride(0) if rows > 1 else n
     if valid_len is not None:
-        _need(valid_len.dtype == torch.int32 and valid_len.shape == (rows,) and valid_len.is_contiguous()
-              and valid_len.device == scores.device, "valid_len must be contiguous int32 [rows]")
+        _need(valid_len.dtype == torch.int32 and valid_len.shape == (rows,) and valid_len.is_contiguous(),
+              "valid_len must be contiguous int32 [rows]")
     if idx_out is None:
         idx_out = torch.empty((rows, k), dtype=torch.int32, device=scores.device)
     if count_out is None:
         count_out = torch.empty((rows,), dtype=torch.int32, device=scores.device)
-    _need(idx_out.shape == (rows, k) and idx_out.dtype == torch.int32 and idx_out.is_contiguous(), "idx_out")
-    _need(count_out.shape == (rows,) and count_out.dtype == torch.int32, "count_out")
+    _need(idx_out.shape == (rows, k) and idx_out.dtype == torch.int32 and idx_out.is_contiguous(),
+          "idx_out must be contiguous int32 [rows, k]")
+    _need(count_out.shape == (rows,) and count_out.dtype == torch.int32 and count_out.is_contiguous(),
+          "count_out must be contiguous int32 [rows]")
     rc = lib.sparse_attn_topk(_ptr(scores), rows, n, ld, _ptr(valid_len), int(k), _ptr(idx_out),
                               _ptr(count_out), None, 0, _stream(scores))
     _lib.check(rc, "sparse_attn_topk", lib)
@@ -121,10 +144,12 @@ def topk(scores: torch.Tensor, k: int, valid_len: Optional[torch.Tensor] = None,
 def pad_heads(q: torch.Tensor, sinks: torch.Tensor, h_pad: int, q_pad: Optional[torch.Tensor] = None,
               s_pad: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """sparse_attn_pad_heads: q [R, h, 512] -> [R, h_pad, 512] with zero heads; sinks -> zero-padded."""
-    lib = load()
+    _need(q.dim() == 3, "q must be [rows, h, D]")
     rows, h, D = q.shape
-    _need(q.is_cuda and q.is_contiguous() and sinks.is_contiguous() and sinks.dtype == torch.float32,
-          "q and sinks must be contiguous device tensors, sinks float32")
+    _on_device(q, "q", sinks=sinks, q_pad=q_pad, s_pad=s_pad)
+    lib = load()
+    _need(q.is_contiguous() and sinks.is_contiguous() and sinks.dtype == torch.float32 and sinks.shape == (h,),
+          "q must be contiguous, sinks contiguous float32 [h]")
     if q_pad is None:
         q_pad = torch.empty((rows, h_pad, D), dtype=q.dtype, device=q.device)
     if s_pad is None:
@@ -139,10 +164,11 @@ def pad_heads(q: torch.Tensor, sinks: torch.Tensor, h_pad: int, q_pad: Optional[
 
 def unpad_heads(out_pad: torch.Tensor, h_real: int, out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """sparse_attn_unpad_heads: heads 0..h_real-1 of out_pad [R, h_pad, 512] (float32)."""
-    lib = load()
+    _need(out_pad.dim() == 3, "out_pad must be [rows, h_pad, D]")
     rows, h_pad, D = out_pad.shape
-    _need(out_pad.is_cuda and out_pad.is_contiguous() and out_pad.dtype == torch.float32,
-          "out_pad must be a contiguous float32 device tensor")
+    _on_device(out_pad, "out_pad", out=out)
+    lib = load()
+    _need(out_pad.is_contiguous() and out_pad.dtype == torch.float32, "out_pad must be contiguous float32")
     if out is None:
         out = torch.empty((rows, h_real, D), dtype=torch.float32, device=out_pad.device)
     _need(out.shape == (rows, h_real, D) and out.dtype == torch.float32 and out.is_contiguous(), "out")

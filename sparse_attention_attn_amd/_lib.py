@@ -14,7 +14,8 @@ LIB_PATH = os.path.join(HERE, "libsparse_attn.so")
 SA_OK, SA_ERR_NULL, SA_ERR_SHAPE, SA_ERR_UNSUPPORTED, SA_ERR_WORKSPACE, SA_ERR_HIP = range(6)
 SA_F32, SA_BF16 = 0, 1
 SA_OP_DECODE, SA_OP_PREFILL, SA_OP_TOPK = 0, 1, 2
-SA_HEAD_DIM, SA_MAX_HEADS, SA_BF16_MAX_CTX = 512, 128, 4194303
+SA_HEAD_DIM, SA_MAX_HEADS, SA_BF16_MAX_CTX, SA_MAX_KMAX = 512, 128, 4194303, 1 << 24
+SA_ABI_VERSION = 2
 
 _c = ctypes
 _P = _c.c_void_p
@@ -57,6 +58,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         fn = getattr(lib, name)
         fn.restype = res
         fn.argtypes = args
+    if lib.sparse_attn_abi_version() != SA_ABI_VERSION:
+        raise RuntimeError(f"{path} has ABI version {lib.sparse_attn_abi_version()}, this binding "
+                           f"expects {SA_ABI_VERSION}; rebuild it")
     if path == LIB_PATH:
         _lib = lib
     return lib

@@ -52,7 +52,6 @@ constexpr int64_t kMaxGrid = 0x7fffffff;
 int check_attn(int dtype, const void *q, const void *k, const void *v, int64_t n_ctx, const int32_t *idx,
                const int32_t *nsel, int32_t kmax, const float *sinks, float scale, int32_t rows, int32_t H,
                int32_t D, float *out, void *ws, size_t ws_bytes, bool shared) {
-    (void)ws;
     (void)nsel;
     (void)scale;
     if (rows > 0 && (!q || !k || !v || !idx || !sinks || !out))
@@ -61,7 +60,7 @@ int check_attn(int dtype, const void *q, const void *k, const void *v, int64_t n
     if (D != SA_HEAD_DIM) return fail(SA_ERR_UNSUPPORTED, "head width %d: only %d is implemented", D, SA_HEAD_DIM);
     if (H < 1 || H > SA_MAX_HEADS) return fail(SA_ERR_SHAPE, "heads %d outside [1, %d]", H, SA_MAX_HEADS);
     if (rows < 0) return fail(SA_ERR_SHAPE, "row count %d is negative", rows);
-    if (kmax < 1) return fail(SA_ERR_SHAPE, "kmax %d must be >= 1", kmax);
+    if (kmax < 1 || kmax > SA_MAX_KMAX) return fail(SA_ERR_SHAPE, "kmax %d outside [1, %d]", kmax, SA_MAX_KMAX);
     if (n_ctx < 1 || n_ctx > 0x7fffffff) return fail(SA_ERR_SHAPE, "n_ctx %lld outside [1, 2^31)", (long long)n_ctx);
     const int64_t elt = dtype == SA_BF16 ? 2 : 4;
     const int64_t caches = shared ? 1 : rows;
@@ -70,18 +69,22 @@ int check_attn(int dtype, const void *q, const void *k, const void *v, int64_t n
         return fail(SA_ERR_UNSUPPORTED, "q, k_cache, v_cache and out must be 16-byte aligned");
     if (!aligned(idx, 4) || !aligned(sinks, 4) || (nsel && !aligned(nsel, 4)))
         return fail(SA_ERR_UNSUPPORTED, "idx, nsel and sinks must be 4-byte aligned");
+    size_t need = 0;
     if (dtype == SA_BF16) {
         // The gathers address a cache through a 32-bit byte range (1 KiB per position).
         if (n_ctx > SA_BF16_MAX_CTX)
             return fail(SA_ERR_UNSUPPORTED, "n_ctx %lld: bf16 caches hold at most %d positions", (long long)n_ctx,
                         SA_BF16_MAX_CTX);
-        const sa::AttnPlan p = sa::plan_attn_bf16(rows, H);
+        const sa::AttnPlan p = sa::plan_attn_bf16(rows, H, kmax);
         if (p.units > kMaxGrid) return fail(SA_ERR_SHAPE, "too many rows for one launch");
+        need = p.ws_bytes;
     } else if ((int64_t)rows * H > kMaxGrid) {
         return fail(SA_ERR_SHAPE, "too many rows for one launch");
     }
-    const size_t need = sparse_attn_workspace_bytes(shared ? SA_OP_PREFILL : SA_OP_DECODE, rows, H, D, kmax, n_ctx);
+    (void)shared;
     if (ws_bytes < need) return fail(SA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+    if (need > 0 && !ws) return fail(SA_ERR_NULL, "this launch needs a workspace of %zu bytes", need);
+    if (need > 0 && !aligned(ws, 16)) return fail(SA_ERR_UNSUPPORTED, "the workspace must be 16-byte aligned");
     return SA_OK;
 }
 
@@ -104,6 +107,7 @@ int run_attn(int dtype, const void *q, const void *k, const void *v, int64_t n_c
     a.rows = rows;
     a.H = H;
     a.out = out;
+    a.ws = ws;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const hipError_t e = dtype == SA_BF16 ? sa::launch_attn_bf16(a, s) : sa::launch_attn_f32(a, s);
     if (e != hipSuccess) return fail(SA_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
@@ -132,13 +136,11 @@ const char *sparse_attn_last_error(void) { return g_last_error; }
 
 size_t sparse_attn_workspace_bytes(int op, int64_t rows, int32_t heads, int32_t head_dim, int32_t kmax,
                                    int64_t n_ctx) {
-    (void)op;
-    (void)rows;
-    (void)heads;
     (void)head_dim;
-    (void)kmax;
     (void)n_ctx;
-    return 0;
+    if (op != SA_OP_DECODE && op != SA_OP_PREFILL) return 0;
+    if (rows <= 0 || heads < 1 || heads > SA_MAX_HEADS || kmax < 1 || kmax > SA_MAX_KMAX) return 0;
+    return sa::plan_attn_bf16(rows, heads, kmax).ws_bytes;
 }
 
 int sparse_attn_decode(int dtype, const void *q, const void *k_cache, const void *v_cache, int64_t n_ctx,

@@ -48,126 +48,12 @@
 
 #include <type_traits>
 
+#include "sa_attn_common.h"
 #include "sa_device.h"
 #include "sa_internal.h"
 
 namespace sa {
 namespace {
-
-constexpr int kWaves = 8;
-constexpr int kRows = kTile / kWaves;   // rows each wave gathers per tile (per buffer)
-
-// K slot, within a 32-key half, of key kap = 8g + 4b + r: slot 16b + 4g + r. Row 4g + r of
-// the score MFMA over slots 16b .. 16b+15 lands in lane group g, element r, which is the
-// P^T operand's element 4b + r (key 8g + 4b + r).
-__device__ __forceinline__ int kslot_of_key(int kap) { return ((kap & 4) << 2) | ((kap >> 3) << 2) | (kap & 3); }
-
-// LDS row stride of the separate kernel's V buffer: the row bytes plus 32, an odd multiple
-// of 32 for every slice width. A transposing read of the value MFMA's operand touches
-// eight consecutive V slots (V slot of key kap: swap23(kap)) at one 32-byte column
-// window; with an odd multiple of 32 as stride they land on eight different bank windows.
-constexpr int vstride_of(int vrow) { return vrow + 32; }
-
-// Chunk swizzle of the aliased kernel's tile rows (stride 1024): the 16-byte chunk c of
-// the row in slot s is stored at chunk c ^ tswz(s). The score reads (sixteen slots
-// 16b .. 16b+15, one chunk) see sixteen different values of tswz and so sixteen bank
-// groups; the value reads (slots 16t2 + 0..7, or + 8..15, one aligned 32-byte window) see
-// eight different even (or odd) values, which keep each window whole and move the eight
-// windows to eight different places.
-__device__ __forceinline__ int tswz(int s) { return ((s & 7) << 1) | ((s >> 3) & 1); }
-
-template <typename T>
-__device__ __forceinline__ const SA_LDS T *lds_at(uint32_t addr) {
-    return (const SA_LDS T *)(uintptr_t)addr;
-}
-
-// Online-softmax state of one wave over its key half, relative to the reference ref.
-struct HalfState {
-    float m, ref, l;
-};
-
-template <int CB>
-__device__ __forceinline__ void half_start(HalfState &st, f32x4 (&acc)[CB], bool with_sink, float sink) {
-    if (with_sink) {
-        const float sink2 = sink * kLog2e;
-        st.m = sink2;
-        st.ref = (sink2 == -INFINITY) ? 0.0f : sink2;
-        st.l = exp2_hw(sink2 - st.ref);
-    } else {
-        st.m = -INFINITY;
-        st.ref = 0.0f;
-        st.l = 0.0f;
-    }
-#pragma unroll
-    for (int cb = 0; cb < CB; cb++) acc[cb] = (f32x4){};
-}
-
-// One half tile. s0, s1: the score MFMA blocks; element 4b + r of this lane is key p0 + 4b
-// + r of the row's list (p0 = 64 tile + 32 kh + 8 g); keys at or past n are masked (whole:
-// the tile lies inside the row's count, so nothing is). Returns the two bf16 parts of the
-// weights as the P^T operand, and updates the state and acc.
-template <int CB>
-__device__ __forceinline__ void half_tile(const f32x4 &s0, const f32x4 &s1, int p0, int n, bool whole, float scale2,
-                                          HalfState &st, f32x4 (&acc)[CB], bf16x8 &ph, bf16x8 &pl) {
-    float s[8];
-    float mloc = -INFINITY;
-    if (whole) {
-#pragma unroll
-        for (int e = 0; e < 8; e++) {
-            s[e] = (e < 4 ? s0[e] : s1[e - 4]) * scale2;
-            mloc = fmaxf(mloc, s[e]);
-        }
-    } else {
-#pragma unroll
-        for (int e = 0; e < 8; e++) {
-            const float full = e < 4 ? s0[e] : s1[e - 4];
-            s[e] = p0 + e < n ? full * scale2 : -INFINITY;
-            mloc = fmaxf(mloc, s[e]);
-        }
-    }
-    mloc = max_xor32(max_xor16(mloc));
-    const float m_new = fmaxf(st.m, mloc);
-    // The reference follows the running maximum lazily: it moves (and l, acc are rescaled
-    // by alpha) only when the maximum has risen more than kLazy above it, or when it sits
-    // above a finite maximum (from the start value 0); the decision is taken for the
-    // wave's 16 heads together. Otherwise alpha = 1 and every p stays <= 2^kLazy.
-    const bool move = m_new > st.ref + kLazy || (m_new < st.ref && m_new != -INFINITY);
-    const bool rescale = __builtin_amdgcn_ballot_w64(move) != 0;
-    float alpha = 1.0f;
-    if (rescale) {
-        const float ref_new = (m_new == -INFINITY) ? 0.0f : m_new;
-        // Nothing accumulated yet (l = 0): the old reference may be arbitrarily far from
-        // the new one, and 0 (not 2^(r - r'), which can overflow) keeps acc at 0.
-        alpha = st.l == 0.0f ? 0.0f : exp2_hw(st.ref - ref_new);
-        st.ref = ref_new;
-    }
-    // p = hi + lo with both parts bf16, so the value product (one MFMA per part) sees p
-    // to about 16 significant bits and l sums the same hi + lo. hi is p truncated toward
-    // zero and lo = bf16(p - hi); when p is itself a positive bf16 value, hi is the next
-    // bf16 below it and lo its last unit, so hi + lo = p exactly, and an infinite value
-    // times a positive weight stays infinite. For p >= 0 both cases are the top half of
-    // bits(p) - 1, saturated at 0 (p = 0 gives hi = lo = 0; a NaN stays a NaN).
-    float psum = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 8; e++) {
-        const float pf = exp2_hw(s[e] - st.ref);
-        const uint32_t pbits = __float_as_uint(pf);
-        const uint32_t hb = __builtin_elementwise_sub_sat(pbits, 1u);
-        const float hif = __uint_as_float(hb & 0xffff0000u);
-        const __bf16 hi = __builtin_bit_cast(__bf16, (uint16_t)(hb >> 16));
-        const __bf16 lo = (__bf16)(pf - hif);
-        psum += hif + (float)lo;
-        ph[e] = hi;
-        pl[e] = lo;
-    }
-    psum = sum_xor32(sum_xor16(psum));
-    st.l = __builtin_fmaf(alpha, st.l, psum);
-    st.m = m_new;
-    if (rescale) [[unlikely]] {
-#pragma unroll
-        for (int cb = 0; cb < CB; cb++) acc[cb] *= alpha;
-    }
-}
 
 // Row rotation by 8 inside each 16-lane row (DPP row_ror:8): lane l16 receives lane l16 ^ 8.
 __device__ __forceinline__ float ror8(float x) {
@@ -196,8 +82,8 @@ __device__ __forceinline__ void combine_store(const HalfState &st, const f32x4 (
         meta[w][1][l16] = st.ref;
         meta[w][2][l16] = st.l;
     }
-    // x * 1 is x exactly and x * NaN is NaN: a select of constants, so the divide is not
-    // put behind a branch and the store count stays the same on every path.
+    // x * 1 is x exactly and x * NaN is NaN: a select of constants, so the store count stays
+    // the same on every path.
     const float poison = bad ? NAN : 1.0f;
     const bool lo_row = l16 < 8;
     // Output addresses. One block: head head0 + l16, columns col0 + 16cb + 4g. A pair:
@@ -208,7 +94,7 @@ __device__ __forceinline__ void combine_store(const HalfState &st, const f32x4 (
     const int baseA = hA < H ? (hA * kHeadDim + col0 + 4 * (g + 4 * (l16 >> 3))) * 4 : -1;
     const int baseB = hB < H ? (hB * kHeadDim + col0 + 4 * (g + 4 * (l16 >> 3))) * 4 : -1;
     auto at = [](int base, int bytes) { return base < 0 ? kDropOffset : base + bytes; };
-    float a0 = 0.0f, a1 = 0.0f, lsum = 1.0f;
+    HalfFold fold{0.0f, 0.0f, 1.0f};
 #pragma unroll
     for (int r = 0; r < 2; r++) {
         // Round 0: every wave is past its value products (the buffer is free).
@@ -222,12 +108,7 @@ __device__ __forceinline__ void combine_store(const HalfState &st, const f32x4 (
             const float mp = meta[p][0][l16], rp = meta[p][1][l16], lp = meta[p][2][l16];
             const float m0 = KH ? mp : st.m, r0 = KH ? rp : st.ref, l0 = KH ? lp : st.l;
             const float m1 = KH ? st.m : mp, r1 = KH ? st.ref : rp, l1 = KH ? st.l : lp;
-            const float R = m0 >= m1 ? r0 : r1;
-            a0 = l0 == 0.0f ? 0.0f : exp2_hw(r0 - R);
-            a1 = l1 == 0.0f ? 0.0f : exp2_hw(r1 - R);
-            // Explicit fused forms: the order of the two products is fixed, whatever
-            // contraction the compiler would choose in each instance.
-            lsum = __builtin_fmaf(a0, l0, a1 * l1);
+            fold = fold_scales(m0, r0, l0, m1, r1, l1);
         }
         auto finish = [&](int cb, const f32x4 &par) {
             const f32x4 own = acc[cb];
@@ -235,7 +116,7 @@ __device__ __forceinline__ void combine_store(const HalfState &st, const f32x4 (
             const f32x4 x1 = KH ? own : par;
             f32x4 o;
 #pragma unroll
-            for (int e = 0; e < 4; e++) o[e] = (__builtin_fmaf(a0, x0[e], a1 * x1[e]) / lsum) * poison;
+            for (int e = 0; e < 4; e++) o[e] = fold_elem(fold, x0[e], x1[e], poison);
             return o;
         };
         // The partner reads go out four at a time ahead of their first use, so their LDS
@@ -335,27 +216,6 @@ __device__ __forceinline__ int resolve(const AttnArgs &a, const Item &it, const 
     return (live && inr) ? iv : -1;
 }
 
-// The next unit's query and sink, loaded asynchronously into qreg (the previous unit's last
-// scores have been formed by then); usable after a wait that covers them and register_ready.
-// Lane (g, l16) holds head head0 + l16, dims 32kk + 8g + 0..7 for kk < 16. Heads
-// past H read zeros (query and sink) from the static zero row.
-__device__ __forceinline__ void load_q_async(const AttnArgs &a, const Item &it, int head0, int g, int l16,
-                                             bf16x8 (&qreg)[16], float &sink) {
-    const int head = head0 + l16;
-    const bool ok = head < a.H;
-    const uint16_t *qrow =
-        ok ? (const uint16_t *)a.q + (it.row * a.H + head) * kHeadDim : (const uint16_t *)g_zero_row;
-    qrow += 8 * g;
-#pragma unroll
-    for (int kk = 0; kk < 16; kk++) load16_async(qreg[kk], qrow + 32 * kk);
-    load4_async(sink, ok ? a.sinks + head : (const float *)g_zero_row);
-}
-__device__ __forceinline__ void q_ready(bf16x8 (&qreg)[16], float &sink) {
-#pragma unroll
-    for (int kk = 0; kk < 16; kk++) register_ready(qreg[kk]);
-    register_ready(sink);
-}
-
 // ---------------------------------------------------------------------------------------
 // Separate K and V caches. One K buffer and one V buffer of 64 rows each: V(j) is gathered
 // while the scores of tile j run, K(j+1) while its values are applied. Two barriers per
@@ -442,7 +302,7 @@ attn_bf16_kernel(AttnArgs a, int n_hg, int64_t units) {
     Item nx = str.next(cur);
     Item nx2 = str.next(nx);
     bool bad = false, bad_next = false;
-    load_q_async(a, cur, cur.hg * 16 * HQ + 16 * hq, g, l16, qreg, sink_n);
+    load_q_async(a, cur.row, cur.hg * 16 * HQ + 16 * hq, g, l16, qreg, sink_n);
     dma_idx(a, cur, cur, &idx_lds[w][0][0], lane);
     wait_vmcnt<0>();
     q_ready(qreg, sink_n);
@@ -479,27 +339,14 @@ attn_bf16_kernel(AttnArgs a, int n_hg, int64_t units) {
         lds_barrier();  // every wave's K(j) has landed; every wave is done with V(j-1)
 
         // ---- scores of the wave's 32 keys for its 16 heads over the full head width.
-        f32x4 sacc0 = (f32x4){}, sacc1 = (f32x4){};
+        f32x4 sacc0, sacc1;
         {
+            // The tile's V rows go out in the score steps, one every two, in the matrix pipe's
+            // shadow (every wave finished the previous tile's values before the barrier).
             const __amdgpu_buffer_rsrc_t rv = rsrc_v(cur);
-            bf16x8 k0 = *(const SA_LDS bf16x8 *)(krow);
-            bf16x8 k1 = *(const SA_LDS bf16x8 *)(krow + 16 * kKStride);
-#pragma unroll
-            for (int kk = 0; kk < 16; kk++) {
-                bf16x8 n0 = k0, n1 = k1;
-                if (kk + 1 < 16) {
-                    n0 = *(const SA_LDS bf16x8 *)(krow + 64 * (kk + 1));
-                    n1 = *(const SA_LDS bf16x8 *)(krow + 16 * kKStride + 64 * (kk + 1));
-                }
-                sacc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qreg[kk], sacc0, 0, 0, 0);
-                sacc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qreg[kk], sacc1, 0, 0, 0);
-                // The tile's V rows go out here, one every two steps, in the matrix pipe's
-                // shadow (every wave finished the previous tile's values before the barrier).
+            score_chain(krow, qreg, sacc0, sacc1, [&](int kk) {
                 if (kk % 2 == 0) dma_v_row(rv, iv_cur, kk / 2);
-                __builtin_amdgcn_sched_barrier(0);
-                k0 = n0;
-                k1 = n1;
-            }
+            });
         }
 
         // Indices of item j+1 have landed (after them: [stores], V(j)).
@@ -527,7 +374,7 @@ attn_bf16_kernel(AttnArgs a, int n_hg, int64_t units) {
         if (shared_cache && more) wait_vmcnt<2>(); else wait_vmcnt<0>();
         // On a unit's last tile: the next unit's query (the scores were qreg's last use),
         // ahead of the K rows, so the wait for K(j+1) covers it too.
-        if (q_now) load_q_async(a, nx, nx.hg * 16 * HQ + 16 * hq, g, l16, qreg, sink_n);
+        if (q_now) load_q_async(a, nx.row, nx.hg * 16 * HQ + 16 * hq, g, l16, qreg, sink_n);
         lds_barrier();  // every wave's V(j) has landed; every wave is done with K(j)
 
         // ---- values O^T += V^T P^T over the wave's 32 keys, one MFMA per part of P.
@@ -656,7 +503,7 @@ attn_bf16_alias_kernel(AttnArgs a, int n_hg, int64_t units) {
         bad1 = bad1 || (b && d == 1);
         bad2 = bad2 || (b && d == 2);
     };
-    load_q_async(a, cur, cur.hg * 16 * HQ + 16 * hq, g, l16, qreg, sink_n);
+    load_q_async(a, cur.row, cur.hg * 16 * HQ + 16 * hq, g, l16, qreg, sink_n);
     dma_idx(a, cur, cur, &idx_lds[w][0][0], lane);
     dma_idx(a, nx, cur, &idx_lds[w][1][0], lane);
     wait_vmcnt<0>();
@@ -719,7 +566,7 @@ attn_bf16_alias_kernel(AttnArgs a, int n_hg, int64_t units) {
             }
         }
         // The scores were the last use of qreg in this unit.
-        if (q_now) load_q_async(a, nx, nx.hg * 16 * HQ + 16 * hq, g, l16, qreg, sink_n);
+        if (q_now) load_q_async(a, nx.row, nx.hg * 16 * HQ + 16 * hq, g, l16, qreg, sink_n);
 
         bf16x8 ph, pl;
         half_tile(sacc0, sacc1, cur.tile * kTile + 32 * kh + 8 * g, cur.n, (cur.tile + 1) * kTile <= cur.n, scale2,
@@ -829,8 +676,15 @@ constexpr int kSmallLds = kWaves * 2 * 64 * 4 + kWaves * 3 * 16 * 4;
 
 }  // namespace
 
-AttnPlan plan_attn_bf16(int64_t rows, int H) {
+AttnPlan plan_attn_bf16(int64_t rows, int H, int32_t kmax) {
     AttnPlan p{};
+    const int64_t n_hb = (H + 63) / 64;
+    if (kmax <= kSplitMaxK && rows * n_hb < kSplitMaxUnits) {
+        p.split = 1;
+        p.threads = 512;
+        p.ws_bytes = split_workspace_bytes(rows, H, kmax);
+        return p;
+    }
     const int hq = H > 32 ? 4 : (H > 16 ? 2 : 1);
     p.heads_per_wg = 16 * hq;
     const int64_t n_hg = (H + p.heads_per_wg - 1) / p.heads_per_wg;
@@ -854,7 +708,8 @@ AttnPlan plan_attn_bf16(int64_t rows, int H) {
 }
 
 hipError_t launch_attn_bf16(const AttnArgs &a, hipStream_t s) {
-    const AttnPlan p = plan_attn_bf16(a.rows, a.H);
+    const AttnPlan p = plan_attn_bf16(a.rows, a.H, a.kmax);
+    if (p.split) return launch_attn_split(a, s);
     if (p.units == 0) return hipSuccess;
     return a.k == a.v ? launch_plan<true>(a, p, s) : launch_plan<false>(a, p, s);
 }

@@ -22,6 +22,7 @@ struct AttnArgs {
     int32_t rows;
     int32_t H;
     float *out;             // [rows, H, 512]
+    void *ws;               // workspace of the split path (score tiles), or nullptr
 };
 
 struct TopkArgs {
@@ -44,18 +45,30 @@ hipError_t launch_pad_heads(int dtype, const void *q, int64_t rows, int h_real, 
 hipError_t launch_unpad_heads(const float *out_pad, int64_t rows, int h_pad, int h_real, float *out,
                               hipStream_t s);
 
-// Launch geometry of the bf16 attention kernel for a given problem (exposed for the
-// host-side tests through sparse_attn_plan in the API layer).
+// Launch geometry of the bf16 attention for a given problem. Small batches take the split
+// path (sa_attn_split.hip): the score contraction of every 64-key tile in its own workgroup,
+// the scores through the workspace, then the softmax and values per (row, 16-head group,
+// 64-column slice). Larger ones take the persistent kernels (sa_attn.hip). Both give the same
+// bits, so the choice is free to follow the batch size.
 struct AttnPlan {
-    int heads_per_wg;       // 16, 32 or 64
-    int cols_per_wg;        // 64, 128, 256 or 512
-    int64_t units;          // (row, head group, column slice) work units; the launch runs
-                            // min(units, compute units) persistent workgroups over them
+    int split;              // 1: the split path
+    int heads_per_wg;       // persistent kernels: 16, 32 or 64
+    int cols_per_wg;        // persistent kernels: 64, 128, 256 or 512
+    int64_t units;          // persistent kernels: (row, head group, column slice) work units; the
+                            // launch runs min(units, compute units) workgroups over them
     int threads;            // per workgroup
     int lds_bytes;          // static LDS per workgroup, separate K and V caches
     int lds_bytes_aliased;  // the same for one cache serving as both
+    size_t ws_bytes;        // workspace the launch needs (0 for the persistent kernels)
 };
-AttnPlan plan_attn_bf16(int64_t rows, int H);
+// The split path takes rows whose index lists hold at most kSplitMaxK entries (the values
+// kernel keeps a row's list in LDS), when fewer than kSplitMaxUnits (row, 64-head block) pairs
+// would leave most compute units of the persistent grid idle.
+constexpr int kSplitMaxK = 1024;
+constexpr int64_t kSplitMaxUnits = 64;
+AttnPlan plan_attn_bf16(int64_t rows, int H, int32_t kmax);
+size_t split_workspace_bytes(int64_t rows, int H, int32_t kmax);
+hipError_t launch_attn_split(const AttnArgs &a, hipStream_t s);
 
 // Compute units of the current device, cached per device (256 if the query fails).
 int device_cu_count();

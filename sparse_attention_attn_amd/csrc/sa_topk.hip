@@ -186,7 +186,7 @@ __device__ __forceinline__ void topk_regs_row(TopkArgs a) {
     static_assert(kBinsPerThread % 4 == 0, "bins are read and cleared 16 bytes at a time");
     __shared__ uint32_t cnt_lds[2][WAVES];
     __shared__ __attribute__((aligned(16))) uint32_t hist[kBins];
-    __shared__ uint32_t pick_lds[3];
+    __shared__ uint32_t pick_lds[4];  // digit, count above it, count in it; T (early exit)
     constexpr int kStage = 4096;
     __shared__ int32_t out_lds[kStage + 64];
 
@@ -286,13 +286,14 @@ __device__ __forceinline__ void topk_regs_row(TopkArgs a) {
         t_count = pick_lds[2];
         // One key has the digits found so far: it is T (and krem = 1). Its owner publishes
         // it, which replaces the remaining passes. (Not with 64 keys per lane, where the
-        // extra loop costs more registers than the pass it saves.)
+        // extra loop costs more registers than the pass it saves.) It goes to its own slot:
+        // other waves may still be reading slot 0 of this pass.
         if (KPL <= 16 && pass < 2 && t_count == 1u) {
 #pragma unroll
             for (int r = 0; r < KPL; r++)
-                if ((base + 64 * r < vl) & ((key[r] >> shift) == prefix)) pick_lds[0] = key[r];
+                if ((base + 64 * r < vl) & ((key[r] >> shift) == prefix)) pick_lds[3] = key[r];
             __syncthreads();
-            prefix = pick_lds[0];
+            prefix = pick_lds[3];
             break;
         }
     }

@@ -26,9 +26,11 @@ def test_header_and_binding_agree():
 
 def test_header_constants_match_binding():
     text = open(HEADER).read()
-    for name in ("SA_HEAD_DIM", "SA_MAX_HEADS", "SA_BF16_MAX_CTX"):
+    for name in ("SA_HEAD_DIM", "SA_MAX_HEADS", "SA_BF16_MAX_CTX", "SA_ABI_VERSION"):
         m = re.search(r"#define\s+%s\s+(\d+)" % name, text)
         assert m and int(m.group(1)) == getattr(L, name), name
+    m = re.search(r"#define\s+SA_MAX_KMAX\s+\(1 << (\d+)\)", text)
+    assert m and 1 << int(m.group(1)) == L.SA_MAX_KMAX
 
 
 def test_every_declared_symbol_is_exported():
@@ -39,16 +41,41 @@ def test_every_declared_symbol_is_exported():
 
 def test_version_and_status_strings():
     lib = L.load()
-    assert lib.sparse_attn_abi_version() == 1
+    assert lib.sparse_attn_abi_version() == L.SA_ABI_VERSION == 2
     for code in range(6):
         assert lib.sparse_attn_status_string(code)
     assert lib.sparse_attn_status_string(99) == b"unknown status"
-    assert lib.sparse_attn_workspace_bytes(L.SA_OP_DECODE, 1024, 64, 512, 640, 4096) == 0
+
+
+@pytest.mark.parametrize("op,rows,heads,kmax,expect", [
+    # large batches: the persistent kernels, no workspace
+    (L.SA_OP_DECODE, 1024, 64, 640, 0),
+    (L.SA_OP_DECODE, 64, 64, 640, 0),
+    (L.SA_OP_DECODE, 32, 128, 640, 0),
+    (L.SA_OP_PREFILL, 2048, 16, 640, 0),
+    # small batches: score tiles of 4 KiB per (row, 64-key tile, 16-head group)
+    (L.SA_OP_DECODE, 1, 64, 640, 1 * 10 * 4 * 4096),
+    (L.SA_OP_DECODE, 8, 64, 641, 8 * 11 * 4 * 4096),
+    (L.SA_OP_DECODE, 63, 64, 1, 63 * 1 * 4 * 4096),
+    (L.SA_OP_PREFILL, 31, 128, 64, 31 * 1 * 8 * 4096),
+    (L.SA_OP_DECODE, 2, 4, 64, 2 * 1 * 1 * 4096),
+    (L.SA_OP_DECODE, 2, 17, 1024, 2 * 16 * 2 * 4096),
+    # index lists longer than 1,024 entries stay on the persistent kernels
+    (L.SA_OP_DECODE, 1, 64, 1025, 0),
+    # top-k and invalid sizes: none
+    (L.SA_OP_TOPK, 1, 64, 640, 0),
+    (L.SA_OP_DECODE, 0, 64, 640, 0),
+    (L.SA_OP_DECODE, 1, 0, 640, 0),
+    (L.SA_OP_DECODE, 1, 64, 0, 0),
+])
+def test_workspace_bytes(op, rows, heads, kmax, expect):
+    lib = L.load()
+    assert lib.sparse_attn_workspace_bytes(op, rows, heads, 512, kmax, 4096) == expect
 
 
 def _decode(lib, **kw):
     args = dict(dtype=L.SA_BF16, q=A16, k=A16, v=A16, n_ctx=4096, idx=A16, nsel=None, kmax=640, sinks=A16,
-                scale=0.044, rows=8, H=64, D=512, out=A16, ws=None, ws_bytes=0, stream=None)
+                scale=0.044, rows=1024, H=64, D=512, out=A16, ws=None, ws_bytes=0, stream=None)
     args.update(kw)
     return lib.sparse_attn_decode(*args.values())
 
@@ -65,6 +92,12 @@ def _decode(lib, **kw):
     (dict(H=129), L.SA_ERR_SHAPE),
     (dict(rows=-1), L.SA_ERR_SHAPE),
     (dict(kmax=0), L.SA_ERR_SHAPE),
+    (dict(kmax=L.SA_MAX_KMAX + 1), L.SA_ERR_SHAPE),
+    (dict(kmax=2 ** 31 - 1), L.SA_ERR_SHAPE),
+    (dict(rows=8, ws=A16, ws_bytes=8 * 10 * 4 * 4096 - 1), L.SA_ERR_WORKSPACE),
+    (dict(rows=8), L.SA_ERR_WORKSPACE),
+    (dict(rows=8, ws=None, ws_bytes=8 * 10 * 4 * 4096), L.SA_ERR_NULL),
+    (dict(rows=8, ws=A16 + 8, ws_bytes=8 * 10 * 4 * 4096), L.SA_ERR_UNSUPPORTED),
     (dict(n_ctx=0), L.SA_ERR_SHAPE),
     (dict(n_ctx=4194304), L.SA_ERR_UNSUPPORTED),  # bf16 caches: at most 2^22 - 1 positions
     (dict(q=A16 + 8), L.SA_ERR_UNSUPPORTED),
@@ -112,6 +145,79 @@ def test_python_binding_refuses_cpu_tensors():
     with pytest.raises(ValueError):
         sa.decode(q, torch.zeros(1, 8, 512, dtype=torch.bfloat16), torch.zeros(1, 8, 512, dtype=torch.bfloat16),
                   torch.zeros(1, 4, dtype=torch.int32), torch.zeros(4), 0.04)
+
+
+@pytest.fixture
+def stub_library(monkeypatch):
+    """The binding with a library object that fails the test if any entry point is reached:
+    every refusal below must happen in argument checking, before a pointer is passed."""
+    import sparse_attention_attn_amd as sa
+
+    class Stub:
+        def __getattr__(self, name):
+            raise AssertionError(f"{name} was called for arguments the binding must refuse")
+
+    monkeypatch.setattr(sa, "load", lambda *a, **k: Stub())
+    return sa
+
+
+def _attn_args(dev_of=None, **over):
+    import torch
+    t = {
+        "q": torch.zeros(2, 4, 512, dtype=torch.bfloat16),
+        "k_cache": torch.zeros(2, 8, 512, dtype=torch.bfloat16),
+        "v_cache": torch.zeros(2, 8, 512, dtype=torch.bfloat16),
+        "idx": torch.zeros(2, 4, dtype=torch.int32),
+        "sinks": torch.zeros(4),
+        "nsel": torch.zeros(2, dtype=torch.int32),
+        "out": torch.zeros(2, 4, 512),
+        "ws": torch.zeros(4096, dtype=torch.uint8),
+    }
+    if dev_of:
+        t[dev_of] = t[dev_of].to("meta")
+    t.update(over)
+    return t
+
+
+@pytest.mark.parametrize("name", ["k_cache", "v_cache", "idx", "sinks", "nsel", "out", "ws"])
+def test_binding_refuses_a_tensor_on_another_device(stub_library, name):
+    """A tensor on another device than q is refused before the library is reached, the outputs
+    and the workspace included (a host pointer must never reach a kernel)."""
+    sa = stub_library
+    t = _attn_args(dev_of=name)
+    with pytest.raises(ValueError, match=name):
+        sa.decode(t["q"], t["k_cache"], t["v_cache"], t["idx"], t["sinks"], 0.04, nsel=t["nsel"], out=t["out"],
+                  ws=t["ws"])
+
+
+def test_binding_refuses_host_tensors_everywhere(stub_library):
+    import torch
+    sa = stub_library
+    t = _attn_args()
+    with pytest.raises(ValueError, match="HIP device"):
+        sa.prefill(t["q"], t["k_cache"][0], t["v_cache"][0], t["idx"], t["sinks"], 0.04)
+    s = torch.zeros(2, 100)
+    with pytest.raises(ValueError, match="HIP device"):
+        sa.topk(s, 10)
+    for name, kw in (("valid_len", dict(valid_len=torch.zeros(2, dtype=torch.int32, device="meta"))),
+                     ("idx_out", dict(idx_out=torch.zeros(2, 10, dtype=torch.int32, device="meta"))),
+                     ("count_out", dict(count_out=torch.zeros(2, dtype=torch.int32, device="meta")))):
+        with pytest.raises(ValueError, match=name):
+            sa.topk(s, 10, **kw)
+    for name, kw in (("sinks", dict(sinks=torch.zeros(4, device="meta"))),
+                     ("q_pad", dict(q_pad=torch.zeros(2, 8, 512, dtype=torch.bfloat16, device="meta"))),
+                     ("s_pad", dict(s_pad=torch.zeros(8, device="meta")))):
+        args = dict(sinks=t["sinks"])
+        args.update(kw)
+        sinks = args.pop("sinks")
+        with pytest.raises(ValueError, match=name):
+            sa.pad_heads(t["q"], sinks, 8, **args)
+    with pytest.raises(ValueError, match="HIP device"):
+        sa.pad_heads(t["q"], t["sinks"], 8)
+    with pytest.raises(ValueError, match="out"):
+        sa.unpad_heads(torch.zeros(2, 8, 512), 4, out=torch.zeros(2, 4, 512, device="meta"))
+    with pytest.raises(ValueError, match="HIP device"):
+        sa.unpad_heads(torch.zeros(2, 8, 512), 4)
 
 
 def test_zero_rows_is_a_noop_with_null_arrays():

@@ -108,13 +108,14 @@ def test_prefill_sampled_rows():
 
 
 def test_prefill_padded_heads():
-    """16 real heads zero-padded into a 32-head launch with zero sinks; only real heads compared.
-
-    The real heads must equal an unpadded 16-head launch bit for bit, and the oracle within tolerance."""
+    """The whole 2,048-row prefill segment (positions 2,048..4,095) with 16 real heads zero-padded
+    into a 32-head launch with zero sinks (TensorFold pull request 1206, "What changes"); only the
+    real heads are compared. The real heads must equal an unpadded 16-head launch bit for bit on
+    every row, and the oracle within tolerance on sampled rows."""
     import sparse_attention_attn_amd as sa
-    c = w.prefill_bf16(seed=3, rows=256, first_pos=2048, heads=16, row_stride=8)
+    c = w.prefill_bf16(seed=3, rows=2048, first_pos=2048, heads=16)
     d = to_device(c, DEV)
-    say("prefill 16 heads padded to 32")
+    say("prefill 2048 rows, 16 heads padded to 32")
     q_pad, s_pad = sa.pad_heads(d["q"], d["sinks"], 32)
     torch.cuda.synchronize()
     assert torch.equal(q_pad[:, 16:].float(), torch.zeros_like(q_pad[:, 16:].float()))
@@ -125,7 +126,7 @@ def test_prefill_padded_heads():
     torch.cuda.synchronize()
     assert torch.equal(real, plain), "padded launch's real heads differ from the unpadded launch"
     assert torch.equal(real, out_pad[:, :16])
-    rows = list(range(0, 256, 17))
+    rows = [0, 1, 2, 255, 256, 511, 777, 1023, 1024, 1500, 1919, 2040, 2045, 2046, 2047] + list(range(37, 2048, 173))
     ref = run_oracle(c, rows=rows)
     st = assert_parity(real.cpu().numpy()[rows], ref[rows], *BF16_TOL, "padded 16->32")
     say(f"  ok {st}")
@@ -274,9 +275,10 @@ def test_determinism_and_guards():
 
 @pytest.mark.parametrize("heads,alias", [(64, False), (32, False), (16, False), (64, True), (16, True)])
 def test_batch_invariance_across_launch_shapes(heads, alias):
-    """A row's bits do not depend on how many rows share the launch: B = 300, 200, 100, 8 and 1
-    select different column slice counts (1, 2, 4 and 8 at 64 heads; at most 4 at 32 heads and
-    2 at 16), which split heads and columns differently, never keys."""
+    """A row's bits do not depend on how many rows share the launch: B = 300, 200 and 100 run the
+    persistent kernels with different column slice counts (1, 2 and 4 at 64 heads), which split
+    heads and columns differently; B = 8 and 1 run the split path (every 64-key tile scored in its
+    own workgroup, the scores folded in key order), which runs the same arithmetic."""
     import sparse_attention_attn_amd as sa
     c = w.decode_bf16(seed=61 + heads, batch=300, heads=heads, n_ctx=1024, k=640)
     d = to_device(c, DEV)

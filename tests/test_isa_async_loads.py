@@ -3,8 +3,9 @@ destination registers fill in asynchronously: the compiler sees a finished value
 load, so nothing stops it from copying or spilling those registers before the data has
 arrived. The kernels are correct only if it never does, i.e. if every instruction that
 touches such a destination comes after an `s_waitcnt vmcnt` (the explicit waits that cover
-the loads). This compiles csrc/sa_attn.hip to gfx950 assembly with the library's own flags
-and checks that, for every kernel, along the code that follows each such load.
+the loads). This compiles csrc/sa_attn.hip and csrc/sa_attn_split.hip to gfx950 assembly
+with the library's own flags and checks that, for every kernel, along the code that follows
+each such load.
 """
 import os
 import re
@@ -84,13 +85,14 @@ def test_parser_finds_an_early_copy():
     assert loads == 2 and len(bad) == 1 and "a2, v156" in bad[0][1]
 
 
-def test_async_query_loads_are_not_touched_before_a_wait(tmp_path):
-    out = tmp_path / "sa_attn.s"
+@pytest.mark.parametrize("src,tag", [("sa_attn.hip", "attn_bf16"), ("sa_attn_split.hip", "attn_split")])
+def test_async_query_loads_are_not_touched_before_a_wait(tmp_path, src, tag):
+    out = tmp_path / (src + ".s")
     cmd = [HIPCC, *B.HIP_FLAGS, *B.COMMON, "--cuda-device-only", "-S",
-           os.path.join(B.CSRC, "sa_attn.hip"), "-o", str(out)]
+           os.path.join(B.CSRC, src), "-o", str(out)]
     subprocess.run(cmd, check=True, capture_output=True)
-    ks = {k: v for k, v in kernels(out.read_text()).items() if "attn_bf16" in k}
-    assert ks, "no bf16 attention kernels in the listing"
+    ks = {k: v for k, v in kernels(out.read_text()).items() if tag in k}
+    assert ks, f"no {tag} kernels in the listing"
     total = 0
     for name, lines in ks.items():
         bad, loads = early_touches(lines)
