@@ -95,7 +95,7 @@ const char *sparse_attn_last_error(void);
  * and after a call mean nothing, and two calls in flight at once on different
  * streams need different workspaces.
  *
- * Small batches (fewer than 64 rows per block of 64 heads, index lists of at most
+ * Small batches (fewer than 24 rows per block of 64 heads, index lists of at most
  * 1,024 entries) split the keys of every row across workgroups: each 64-key tile
  * is scored in its own workgroup and the raw scores go through the workspace
  * (rows x ceil(kmax / 64) x ceil(heads / 16) x 4 KiB), before the softmax and value

@@ -82,9 +82,7 @@ __device__ __forceinline__ void combine_store(const HalfState &st, const f32x4 (
         meta[w][1][l16] = st.ref;
         meta[w][2][l16] = st.l;
     }
-    // x * 1 is x exactly and x * NaN is NaN: a select of constants, so the store count stays
-    // the same on every path.
-    const float poison = bad ? NAN : 1.0f;
+    const uint64_t bad_mask = __builtin_amdgcn_readfirstlane(bad ? 1 : 0) ? ~0ull : 0ull;
     const bool lo_row = l16 < 8;
     // Output addresses. One block: head head0 + l16, columns col0 + 16cb + 4g. A pair:
     // heads head0 + (l16 & 7) and + 8, columns col0 + 32p + 4(g + 4(l16 >> 3)).
@@ -116,7 +114,7 @@ __device__ __forceinline__ void combine_store(const HalfState &st, const f32x4 (
             const f32x4 x1 = KH ? own : par;
             f32x4 o;
 #pragma unroll
-            for (int e = 0; e < 4; e++) o[e] = fold_elem(fold, x0[e], x1[e], poison);
+            for (int e = 0; e < 4; e++) o[e] = fold_elem(fold, x0[e], x1[e], bad_mask);
             return o;
         };
         // The partner reads go out four at a time ahead of their first use, so their LDS
@@ -691,14 +689,15 @@ AttnPlan plan_attn_bf16(int64_t rows, int H, int32_t kmax) {
     const int64_t rows_hg = rows * n_hg;
     // One workgroup per CU fits (the K tile alone is 65 KiB of LDS). With fewer
     // (row, head block) pairs than CUs, column slices add units; every slice gathers the
-    // full K tile but only its own V columns. A wave keeps at least 64 columns, so blocks
-    // of fewer heads (more column parts per wave pair) allow fewer slices.
-    int ns = 1;
-    if (rows_hg < 64) ns = 8;
-    else if (rows_hg < 128) ns = 4;
-    else if (rows_hg < 256) ns = 2;
+    // full K tile but only its own V columns. The slice count is the largest that keeps all
+    // units in one round of workgroups (a unit is a latency-bound chain of tiles, so a second
+    // round costs a whole chain: 72 us at 48 rows with 8 slices, against 39 us at 32 rows).
+    // A wave keeps at least 64 columns, so blocks of fewer heads (more column parts per wave
+    // pair) allow fewer slices. The slice count never changes a result's bits.
+    const int64_t cus = device_cu_count();
     const int ns_max = 2 * hq;
-    if (ns > ns_max) ns = ns_max;
+    int ns = 1;
+    while (ns < ns_max && rows_hg * (2 * ns) <= cus) ns *= 2;
     p.cols_per_wg = kHeadDim / ns;
     p.units = rows_hg * ns;
     p.threads = 512;

@@ -74,15 +74,17 @@ __device__ __forceinline__ void half_start(HalfState &st, f32x4 (&acc)[CB], bool
     for (int cb = 0; cb < CB; cb++) acc[cb] = (f32x4){};
 }
 
-// One half tile. s0, s1: the score MFMA blocks; element 4b + r of this lane is key p0 + 4b
-// + r of the row's list (p0 = 64 tile + 32 kh + 8 g); keys at or past n are masked (whole:
-// the tile lies inside the row's count, so nothing is). Returns the two bf16 parts of the
-// weights as the P^T operand, and updates the state and acc.
-template <int CB>
-__device__ __forceinline__ void half_tile(const f32x4 &s0, const f32x4 &s1, int p0, int n, bool whole, float scale2,
-                                          HalfState &st, f32x4 (&acc)[CB], bf16x8 &ph, bf16x8 &pl) {
+// The pieces of one half tile's online-softmax step, in the order half_tile runs them. The
+// split kernels run the same pieces for a tile spread over waves and phases; every piece
+// computes the same values from the same inputs, so the results are the same bits.
+//
+// Scaled scores (log2 units) of one half tile and their maximum over the wave's 32 keys. s0,
+// s1: the score MFMA blocks; element 4b + r of this lane is key p0 + 4b + r of the row's list
+// (p0 = 64 tile + 32 kh + 8 g); keys at or past n are masked (whole: the tile lies inside the
+// row's count, so nothing is).
+__device__ __forceinline__ float tile_scores(const f32x4 &s0, const f32x4 &s1, int p0, int n, bool whole,
+                                             float scale2, float (&s)[8]) {
 #pragma clang fp contract(off)
-    float s[8];
     float mloc = -INFINITY;
     if (whole) {
 #pragma unroll
@@ -98,32 +100,38 @@ __device__ __forceinline__ void half_tile(const f32x4 &s0, const f32x4 &s1, int 
             mloc = fmaxf(mloc, s[e]);
         }
     }
-    mloc = max_xor32(max_xor16(mloc));
+    return max_xor32(max_xor16(mloc));
+}
+
+// Reference step: the running maximum takes the tile's maximum, and the exponent reference
+// follows it lazily: it moves only when the maximum has risen more than kLazy above it, or
+// when it sits above a finite maximum (from the start value 0); the decision is taken for the
+// wave's 16 heads together (wave-uniform result). Otherwise every p stays <= 2^kLazy. On a
+// move, ref_prev keeps the old reference for the rescale factor.
+__device__ __forceinline__ bool tile_reference(HalfState &st, float mloc, float &ref_prev) {
+#pragma clang fp contract(off)
     const float m_new = fmaxf(st.m, mloc);
-    // The reference follows the running maximum lazily: it moves (and l, acc are rescaled
-    // by alpha) only when the maximum has risen more than kLazy above it, or when it sits
-    // above a finite maximum (from the start value 0); the decision is taken for the
-    // wave's 16 heads together. Otherwise alpha = 1 and every p stays <= 2^kLazy.
     const bool move = m_new > st.ref + kLazy || (m_new < st.ref && m_new != -INFINITY);
     const bool rescale = __builtin_amdgcn_ballot_w64(move) != 0;
-    float alpha = 1.0f;
-    if (rescale) {
-        const float ref_new = (m_new == -INFINITY) ? 0.0f : m_new;
-        // Nothing accumulated yet (l = 0): the old reference may be arbitrarily far from
-        // the new one, and 0 (not 2^(r - r'), which can overflow) keeps acc at 0.
-        alpha = st.l == 0.0f ? 0.0f : exp2_hw(st.ref - ref_new);
-        st.ref = ref_new;
-    }
-    // p = hi + lo with both parts bf16, so the value product (one MFMA per part) sees p
-    // to about 16 significant bits and l sums the same hi + lo. hi is p truncated toward
-    // zero and lo = bf16(p - hi); when p is itself a positive bf16 value, hi is the next
-    // bf16 below it and lo its last unit, so hi + lo = p exactly, and an infinite value
-    // times a positive weight stays infinite. For p >= 0 both cases are the top half of
-    // bits(p) - 1, saturated at 0 (p = 0 gives hi = lo = 0; a NaN stays a NaN).
+    ref_prev = st.ref;
+    if (rescale) st.ref = (m_new == -INFINITY) ? 0.0f : m_new;
+    st.m = m_new;
+    return rescale;
+}
+
+// Weights of one half tile against the reference ref: p = hi + lo with both parts bf16, so the
+// value product (one MFMA per part) sees p to about 16 significant bits, and psum (the tile
+// sum, reduced over the wave's four lane groups) sums the same hi + lo. hi is p truncated
+// toward zero and lo = bf16(p - hi); when p is itself a positive bf16 value, hi is the next
+// bf16 below it and lo its last unit, so hi + lo = p exactly, and an infinite value times a
+// positive weight stays infinite. For p >= 0 both cases are the top half of bits(p) - 1,
+// saturated at 0 (p = 0 gives hi = lo = 0; a NaN stays a NaN).
+__device__ __forceinline__ float tile_weights(const float (&s)[8], float ref, bf16x8 &ph, bf16x8 &pl) {
+#pragma clang fp contract(off)
     float psum = 0.0f;
 #pragma unroll
     for (int e = 0; e < 8; e++) {
-        const float pf = exp2_hw(s[e] - st.ref);
+        const float pf = exp2_hw(s[e] - ref);
         const uint32_t pbits = __float_as_uint(pf);
         const uint32_t hb = __builtin_elementwise_sub_sat(pbits, 1u);
         const float hif = __uint_as_float(hb & 0xffff0000u);
@@ -133,13 +141,42 @@ __device__ __forceinline__ void half_tile(const f32x4 &s0, const f32x4 &s1, int 
         ph[e] = hi;
         pl[e] = lo;
     }
-    psum = sum_xor32(sum_xor16(psum));
+    return sum_xor32(sum_xor16(psum));
+}
+
+// Rescale factor of a tile: 1 without a reference move, else 2^(ref_prev - ref); 0 while
+// nothing has been accumulated (l = 0): the old reference may then be arbitrarily far from
+// the new one, and 0 (not 2^(r - r'), which can overflow) keeps acc at 0.
+__device__ __forceinline__ float tile_alpha(bool rescale, float l, float ref_prev, float ref) {
+#pragma clang fp contract(off)
+    return rescale ? (l == 0.0f ? 0.0f : exp2_hw(ref_prev - ref)) : 1.0f;
+}
+
+// Tile sum step and accumulator rescale (before the tile's value MFMAs).
+template <int CB>
+__device__ __forceinline__ void tile_accumulate(HalfState &st, bool rescale, float alpha, float psum,
+                                                f32x4 (&acc)[CB]) {
+#pragma clang fp contract(off)
     st.l = __builtin_fmaf(alpha, st.l, psum);
-    st.m = m_new;
     if (rescale) [[unlikely]] {
 #pragma unroll
         for (int cb = 0; cb < CB; cb++) acc[cb] *= alpha;
     }
+}
+
+// One half tile: scores, reference, weights, tile sum and rescale. Returns the two bf16 parts
+// of the weights as the P^T operand of the value MFMAs that follow.
+template <int CB>
+__device__ __forceinline__ void half_tile(const f32x4 &s0, const f32x4 &s1, int p0, int n, bool whole, float scale2,
+                                          HalfState &st, f32x4 (&acc)[CB], bf16x8 &ph, bf16x8 &pl) {
+    float s[8];
+    const float mloc = tile_scores(s0, s1, p0, n, whole, scale2, s);
+    float ref_prev;
+    const float l_prev = st.l;
+    const bool rescale = tile_reference(st, mloc, ref_prev);
+    const float alpha = tile_alpha(rescale, l_prev, ref_prev, st.ref);
+    const float psum = tile_weights(s, st.ref, ph, pl);
+    tile_accumulate(st, rescale, alpha, psum, acc);
 }
 
 // The fold of the two key halves' states (half 0, half 1 in that order): R is the reference
@@ -158,11 +195,17 @@ __device__ __forceinline__ HalfFold fold_scales(float m0, float r0, float l0, fl
     f.lsum = __builtin_fmaf(f.a0, l0, f.a1 * l1);
     return f;
 }
-// One output element: (a_0 x_0 + a_1 x_1) / (a_0 l_0 + a_1 l_1), times poison (1, or NaN for a
-// row with an out-of-range index: a select of constants, never a branch around the divide).
-__device__ __forceinline__ float fold_elem(const HalfFold &f, float x0, float x1, float poison) {
+// One output element: (a_0 x_0 + a_1 x_1) / (a_0 l_0 + a_1 l_1), or the quiet NaN 0x7fc00000
+// where bad_mask (all ones or all zeros, in scalar registers) marks a row with an out-of-range index.
+// The select is one v_cndmask_b32 written out, so that the compiler neither branches around
+// the divides (it turns a select of a divide into a branch) nor lets a NaN payload depend on
+// how it lowered the select: every kernel stores the same bits.
+__device__ __forceinline__ float fold_elem(const HalfFold &f, float x0, float x1, uint64_t bad_mask) {
 #pragma clang fp contract(off)
-    return (__builtin_fmaf(f.a0, x0, f.a1 * x1) / f.lsum) * poison;
+    const float v = __builtin_fmaf(f.a0, x0, f.a1 * x1) / f.lsum;
+    float r;
+    asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(r) : "v"(v), "v"(0x7fc00000u), "s"(bad_mask));
+    return r;
 }
 
 // A row's query for one 16-head group and its sink, loaded asynchronously into qreg;

@@ -21,8 +21,9 @@
 //   2. attn_split_values_kernel: one workgroup per (row, 16-head group, 64-column slice). It
 //      loads the row's index list, gathers the V column slices of a round of up to ten tiles
 //      and their score tiles into LDS in one go, then runs, per wave (key half kh = w >> 2,
-//      16-column part w & 3), the same half_tile online softmax and value MFMAs on each tile in
-//      order, and the same fixed-order fold of the two key halves (sa_attn_common.h).
+//      16-column part w & 3), the same online-softmax steps and value MFMAs on each tile in
+//      order (the four waves of a key half share the weights), and the same fixed-order fold of
+//      the two key halves (sa_attn_common.h).
 // Every (row, head, column) thus sees the same operations, on the same operands, in the same
 // order as in the persistent kernels: which path a launch takes never changes its bits.
 #include <hip/hip_runtime.h>
@@ -54,8 +55,10 @@ __device__ __forceinline__ size_t score_block(int64_t row, int tile, int hg, int
     return (((size_t)row * ntiles_max + tile) * n_hg + hg) * (kSTileB / 4);
 }
 
+// The row's count, by a scalar (constant address space) load: it waits on the scalar counter,
+// not on the vector-memory counter that the gathers in flight hold.
 __device__ __forceinline__ int row_count(const AttnArgs &a, int64_t row) {
-    int n = a.nsel ? a.nsel[row] : a.kmax;
+    int n = a.nsel ? *(const __attribute__((address_space(4))) int32_t *)(a.nsel + row) : a.kmax;
     return n < 0 ? 0 : (n > a.kmax ? a.kmax : n);
 }
 
@@ -76,10 +79,10 @@ attn_split_scores_kernel(AttnArgs a, int ntiles_max, int n_hb, int n_hg) {
     const int hb = (int)(b % n_hb);
     const int tile = (int)((b / n_hb) % ntiles_max);
     const int64_t row = b / ((int64_t)n_hb * ntiles_max);
-    const int n = row_count(a, row);
-    if (tile * kTile >= n) return;
     const int hg = 4 * hb + wi;
 
+    // The query, the tile's index list and the row's count go out together (one memory round
+    // trip); a tile past the count then leaves, once its loads have landed.
     bf16x8 qreg[16];
     float sink_unused;
     load_q_async(a, row, 16 * hg, g, l16, qreg, sink_unused);
@@ -88,7 +91,9 @@ attn_split_scores_kernel(AttnArgs a, int ntiles_max, int n_hb, int n_hg) {
         const int pc = p < a.kmax ? p : a.kmax - 1;
         dma4(a.idx + row * a.kmax, (uint32_t)pc * 4u, lds_addr(&idx_lds[w][0]));
     }
+    const int n = row_count(a, row);
     wait_vmcnt<0>();
+    if (tile * kTile >= n) return;
     q_ready(qreg, sink_unused);
     __builtin_amdgcn_s_waitcnt(0);
     // Row to gather for entry tile*64 + lane, or -1 (masked or out of range: gathers zeros,
@@ -121,15 +126,23 @@ attn_split_scores_kernel(AttnArgs a, int ntiles_max, int n_hb, int n_hg) {
 }
 
 // One workgroup per (row, 16-head group, 64-column slice), in an order that keeps the
-// workgroups of one row and head group on one XCD (they read the same score tiles). Wave w:
-// key half kh = w >> 2 and the 16 columns cs*64 + 16(w & 3) .. +15.
+// workgroups of one row and head group on one XCD (they read the same score tiles). Eight
+// waves, two per SIMD: wave w takes key half kh = w >> 2 and the 16 columns cs*64 + 16(w & 3)
+// .. +15 (one MFMA block). The four waves of a key half split a round's tiles for the
+// expensive part of the online softmax (scaled scores, tile maxima, weights), share them
+// through LDS, and each runs the cheap sequential parts (reference scan, tile sums) itself.
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_split_values_kernel(AttnArgs a, int ntiles_max, int n_hg) {
     __shared__ __attribute__((aligned(16))) char v_lds[kRing * kVTileB];
+    // A tile's scores, then (same slot, same lane layout: 32 bytes per lane and key half) its
+    // weights as the two bf16 parts of the value MFMA's P^T operand.
     __shared__ __attribute__((aligned(16))) char s_lds[kRing * kSTileB];
+    __shared__ float mloc_lds[2][kRing][64];   // per key half and tile: the tile's maximum
+    __shared__ float psum_lds[2][kRing][64];   // per key half and tile: the tile sum
     __shared__ int idx_lds[kSplitMaxK];
     __shared__ float meta_lds[4][3][16];
     __shared__ f32x4 xch_lds[4][64];
+    __shared__ int bad_lds[kWaves];
 
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -137,29 +150,45 @@ attn_split_values_kernel(AttnArgs a, int ntiles_max, int n_hg) {
     const int l16 = lane & 15;
     const int cq = w & 3;
     const int kh = w >> 2;
+    // Residue (mod 4) of the round's tiles this wave weighs: the two waves of a SIMD (w and
+    // w ^ 4) take different residues, so every SIMD weighs five of ten tiles.
+    const int qv = (cq + 2 * kh) & 3;
     const int64_t u = xcd_remap(blockIdx.x, gridDim.x);
     const int cs = (int)(u % kSplitSlices);
     const int hg = (int)((u / kSplitSlices) % n_hg);
     const int64_t row = u / ((int64_t)kSplitSlices * n_hg);
+    const int head = 16 * hg + l16;
+
+    // First memory round trip: the first round's score tiles, the row's index list (the first
+    // ntiles_max * 64 entries, the offsets clamped to the row), the sink and the row's count,
+    // all in flight together. Score tiles past the row's count are never written by the
+    // scores kernel; reading them stays inside the workspace, and they are not used.
+    const int nt_first = ntiles_max < kRing ? ntiles_max : kRing;
+    const float *sws = (const float *)a.ws + score_block(row, 0, hg, ntiles_max, n_hg);
+    const uint32_t v_base = lds_addr((SA_LDS char *)v_lds);
+    const uint32_t s_base = lds_addr((SA_LDS char *)s_lds);
+    // Each wave moves 512 bytes of every 4 KiB score tile, in two 256-byte pieces.
+    auto issue_scores = [&](int t, int slot) {
+        const uint32_t off = (uint32_t)t * (uint32_t)(n_hg * kSTileB) + 512u * w + 4u * lane;
+        dma4(sws, off, s_base + slot * kSTileB + 512 * w);
+        dma4(sws, off + 256u, s_base + slot * kSTileB + 512 * w + 256);
+    };
+    for (int i = 0; i < nt_first; i++) issue_scores(i, i);
+    // Index list: wave w moves tiles w and w + 8 (64 entries each) into LDS.
+#pragma unroll
+    for (int r = 0; r < 2; r++) {
+        const int p = (w + 8 * r) * kTile + lane;
+        const int pc = p < a.kmax ? p : a.kmax - 1;
+        dma4(a.idx + row * a.kmax, (uint32_t)pc * 4u, lds_addr(&idx_lds[p - lane]));
+    }
+    float sink;
+    load4_async(sink, head < a.H ? a.sinks + head : (const float *)g_zero_row);
     const int n = row_count(a, row);
     const int ntiles = (n + kTile - 1) / kTile;
-
-    // The row's index list (masked tail entries -1), and whether an entry inside the count is
-    // out of range (then the whole row is NaN, as in the persistent kernels).
-    int bad_local = 0;
-    for (int p = threadIdx.x; p < ntiles * kTile; p += 512) {
-        int iv = -1;
-        if (p < n) {
-            iv = a.idx[row * a.kmax + p];
-            const bool inr = iv >= 0 && (int64_t)iv < a.n_ctx;
-            bad_local |= !inr;
-            iv = inr ? iv : -1;
-        }
-        idx_lds[p] = iv;
-    }
-    const int head = 16 * hg + l16;
-    const float sink = head < a.H ? a.sinks[head] : 0.0f;
-    const bool bad = __syncthreads_or(bad_local) != 0;
+    wait_vmcnt<0>();
+    register_ready(sink);
+    __builtin_amdgcn_s_waitcnt(0);
+    lds_barrier();  // every wave's index pieces have landed
 
     HalfState st;
     f32x4 acc[1];
@@ -183,36 +212,104 @@ attn_split_values_kernel(AttnArgs a, int ntiles_max, int n_hg) {
         const int chunk = 2 * cq + ((l16 & 3) >> 1);
         vaddr[t2] = (uint32_t)(slot * kVRowB + 16 * (chunk ^ vswz(slot)) + 8 * (l16 & 1));
     }
-    const uint32_t v_base = lds_addr((SA_LDS char *)v_lds);
-    const uint32_t s_base = lds_addr((SA_LDS char *)s_lds);
+    // An entry inside the count that is out of range makes the whole row NaN, as in the
+    // persistent kernels (bad_w: one of this wave's entries is); masked entries (past the
+    // count) gather zeros.
+    bool bad_w = false;
 
     for (int t0 = 0; t0 < ntiles; t0 += kRing) {
         const int nt = ntiles - t0 < kRing ? ntiles - t0 : kRing;
-        // Issue the round: per tile three operations per wave (its eight V slices, and 512
-        // bytes of the tile's 4 KiB of scores in two pieces).
-        for (int i = 0; i < nt; i++) {
-            const int t = t0 + i;
-            const int iv = idx_lds[t * kTile + dslot];
-            const uint32_t voff = ((uint32_t)iv << 10) + dchunk;  // iv = -1: past the range, zeros
-            dma16_buf(rv, voff, v_base + i * kVTileB + w * 1024);
-            const float *sblk = (const float *)a.ws + score_block(row, t, hg, ntiles_max, n_hg);
-            dma4(sblk, 512u * w + 4u * lane, s_base + i * kSTileB + 512 * w);
-            dma4(sblk, 512u * w + 256u + 4u * lane, s_base + i * kSTileB + 512 * w + 256);
+        // Second memory round trip: the round's V slices (and, after the first round, its
+        // score tiles). The round's index entries are read from LDS first, so that the gathers
+        // then go out back to back.
+        if (t0 > 0)
+            for (int i = 0; i < nt; i++) issue_scores(t0 + i, i);
+        int raw[kRing];
+#pragma unroll
+        for (int i = 0; i < kRing; i++) {
+            const int p = (t0 + i) * kTile + dslot;
+            raw[i] = (i < nt && p < n) ? idx_lds[p] : -1;
         }
-        for (int i = 0; i < nt; i++) {
-            const int t = t0 + i;
-            wait_vmcnt_dyn(3 * (nt - 1 - i));  // this wave's operations of tile t have landed
-            lds_barrier();                      // and every wave's
-            const SA_LDS f32x4 *sp = lds_at<f32x4>(s_base + i * kSTileB + (kh * 64 + lane) * 32);
-            const f32x4 s0 = sp[0], s1 = sp[1];
-            bf16x8 ph, pl;
-            half_tile(s0, s1, t * kTile + 32 * kh + 8 * g, n, (t + 1) * kTile <= n, scale2, st, acc, ph, pl);
-            const uint32_t vt = v_base + i * kVTileB;
-            const bf16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((SA_LDS bf16x4 *)lds_at<bf16x4>(vt + vaddr[0]));
-            const bf16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((SA_LDS bf16x4 *)lds_at<bf16x4>(vt + vaddr[1]));
-            const bf16x8 vop = (bf16x8){r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]};
-            acc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, ph, acc[0], 0, 0, 0);
-            acc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pl, acc[0], 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < kRing; i++) {
+            if (i < nt) {
+                const int p = (t0 + i) * kTile + dslot;
+                const bool inr = raw[i] >= 0 && (int64_t)raw[i] < a.n_ctx;
+                bad_w = bad_w || __builtin_amdgcn_ballot_w64(p < n && !inr) != 0;
+                const int iv = inr ? raw[i] : -1;  // -1: an offset past the range, zeros
+                dma16_buf(rv, ((uint32_t)iv << 10) + dchunk, v_base + i * kVTileB + w * 1024);
+            }
+        }
+        wait_vmcnt<0>();
+        lds_barrier();  // every wave's slices and score pieces have landed
+
+        // Phase 1: scaled scores and the tile maximum of this wave's tiles of the round (qv,
+        // qv + 4, qv + 8); the maxima go to LDS for the reference scan.
+        constexpr int kMine = (kRing + 3) / 4;
+        float sk[kMine][8];
+#pragma unroll
+        for (int j = 0; j < kMine; j++) {
+            const int i = qv + 4 * j;
+            if (i < nt) {
+                const int t = t0 + i;
+                const SA_LDS f32x4 *sp = lds_at<f32x4>(s_base + i * kSTileB + (kh * 64 + lane) * 32);
+                const f32x4 s0 = sp[0], s1 = sp[1];
+                mloc_lds[kh][i][lane] =
+                    tile_scores(s0, s1, t * kTile + 32 * kh + 8 * g, n, (t + 1) * kTile <= n, scale2, sk[j]);
+            }
+        }
+        lds_barrier();
+        // Phase 2: the reference scan over the round's tiles in key order (every wave of a key
+        // half computes the same values), then the weights of this wave's tiles against their
+        // references, written over their scores.
+        float ref_t[kRing], refp_t[kRing];
+        uint32_t resc = 0;
+#pragma unroll
+        for (int i = 0; i < kRing; i++) {
+            if (i < nt) {
+                float rp;
+                const bool r = tile_reference(st, mloc_lds[kh][i][lane], rp);
+                ref_t[i] = st.ref;
+                refp_t[i] = rp;
+                resc |= (uint32_t)r << i;
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < kMine; j++) {
+            const int i = qv + 4 * j;
+            if (i < nt) {
+                // ref_t[qv + 4j], picked with static indices
+                float ref = ref_t[4 * j];
+#pragma unroll
+                for (int q = 1; q < 4; q++)
+                    if (4 * j + q < kRing && qv == q) ref = ref_t[4 * j + q < kRing ? 4 * j + q : 0];
+                bf16x8 ph, pl;
+                const float psum = tile_weights(sk[j], ref, ph, pl);
+                SA_LDS bf16x8 *pp = (SA_LDS bf16x8 *)lds_at<bf16x8>(s_base + i * kSTileB + (kh * 64 + lane) * 32);
+                pp[0] = ph;
+                pp[1] = pl;
+                psum_lds[kh][i][lane] = psum;
+            }
+        }
+        lds_barrier();
+        // Phase 3: tile sums, rescales and value MFMAs in key order.
+#pragma unroll
+        for (int i = 0; i < kRing; i++) {
+            if (i < nt) {
+                const bool r = (resc >> i) & 1u;
+                const float alpha = tile_alpha(r, st.l, refp_t[i], ref_t[i]);
+                tile_accumulate(st, r, alpha, psum_lds[kh][i][lane], acc);
+                const SA_LDS bf16x8 *pp = lds_at<bf16x8>(s_base + i * kSTileB + (kh * 64 + lane) * 32);
+                const bf16x8 ph = pp[0], pl = pp[1];
+                const uint32_t vt = v_base + i * kVTileB;
+                const bf16x4 r0 =
+                    __builtin_amdgcn_ds_read_tr16_b64_v4bf16((SA_LDS bf16x4 *)lds_at<bf16x4>(vt + vaddr[0]));
+                const bf16x4 r1 =
+                    __builtin_amdgcn_ds_read_tr16_b64_v4bf16((SA_LDS bf16x4 *)lds_at<bf16x4>(vt + vaddr[1]));
+                const bf16x8 vop = (bf16x8){r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]};
+                acc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, ph, acc[0], 0, 0, 0);
+                acc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pl, acc[0], 0, 0, 0);
+            }
         }
         lds_barrier();  // every wave is done with this round's buffers
     }
@@ -226,15 +323,19 @@ attn_split_values_kernel(AttnArgs a, int ntiles_max, int n_hg) {
         }
         xch_lds[cq][lane] = acc[0];
     }
+    if (lane == 0) bad_lds[w] = bad_w;
     lds_barrier();
     if (kh == 0 && head < a.H) {
+        bool bad = false;
+#pragma unroll
+        for (int i = 0; i < kWaves; i++) bad = bad || bad_lds[i] != 0;
+        const uint64_t bad_mask = __builtin_amdgcn_readfirstlane(bad ? 1 : 0) ? ~0ull : 0ull;
         const HalfFold f = fold_scales(st.m, st.ref, st.l, meta_lds[cq][0][l16], meta_lds[cq][1][l16],
                                        meta_lds[cq][2][l16]);
         const f32x4 x1 = xch_lds[cq][lane];
-        const float poison = bad ? NAN : 1.0f;
         f32x4 o;
 #pragma unroll
-        for (int e = 0; e < 4; e++) o[e] = fold_elem(f, acc[0][e], x1[e], poison);
+        for (int e = 0; e < 4; e++) o[e] = fold_elem(f, acc[0][e], x1[e], bad_mask);
         // Lane (g, l16): head 16hg + l16, columns cs*64 + 16cq + 4g + 0..3.
         float *dst = a.out + (row * a.H + head) * kHeadDim + cs * kSplitCols + 16 * cq + 4 * g;
         __builtin_nontemporal_store(o, (f32x4 *)dst);

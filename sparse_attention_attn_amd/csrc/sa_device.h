@@ -111,6 +111,11 @@ __device__ __forceinline__ void dma4(const void *sbase, uint32_t voff, uint32_t 
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
                  ::"s"(lds), "v"(voff), "s"(sbase) : "memory", "m0");
 }
+// Direct-to-LDS load of 16 bytes per lane, from sbase + voff_i to LDS address lds + 16 i.
+__device__ __forceinline__ void dma16(const void *sbase, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 ::"s"(lds), "v"(voff), "s"(sbase) : "memory", "m0");
+}
 // Asynchronous loads into registers: the destination is written when the data
 // returns, which the compiler does not model, so the value may be used only after an
 // explicit vector-memory wait that covers the load, followed by register_ready on it.

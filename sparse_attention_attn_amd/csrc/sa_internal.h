@@ -62,10 +62,13 @@ struct AttnPlan {
     size_t ws_bytes;        // workspace the launch needs (0 for the persistent kernels)
 };
 // The split path takes rows whose index lists hold at most kSplitMaxK entries (the values
-// kernel keeps a row's list in LDS), when fewer than kSplitMaxUnits (row, 64-head block) pairs
-// would leave most compute units of the persistent grid idle.
+// kernel keeps a row's list in LDS), when there are fewer than kSplitMaxUnits (row, 64-head
+// block) pairs: measured on the decode shape (64 heads, k = 640), the two split kernels take
+// 16 us at 1 row, 19 at 8 and 29 at 16 against 31-36 us for the persistent kernels, and break
+// even near 24 rows. This choice depends on the sizes only, never on the device, so that the
+// workspace a call needs does too.
 constexpr int kSplitMaxK = 1024;
-constexpr int64_t kSplitMaxUnits = 64;
+constexpr int64_t kSplitMaxUnits = 24;
 AttnPlan plan_attn_bf16(int64_t rows, int H, int32_t kmax);
 size_t split_workspace_bytes(int64_t rows, int H, int32_t kmax);
 hipError_t launch_attn_split(const AttnArgs &a, hipStream_t s);

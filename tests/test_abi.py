@@ -51,13 +51,14 @@ def test_version_and_status_strings():
     # large batches: the persistent kernels, no workspace
     (L.SA_OP_DECODE, 1024, 64, 640, 0),
     (L.SA_OP_DECODE, 64, 64, 640, 0),
-    (L.SA_OP_DECODE, 32, 128, 640, 0),
+    (L.SA_OP_DECODE, 24, 64, 640, 0),
+    (L.SA_OP_DECODE, 12, 128, 640, 0),
     (L.SA_OP_PREFILL, 2048, 16, 640, 0),
     # small batches: score tiles of 4 KiB per (row, 64-key tile, 16-head group)
     (L.SA_OP_DECODE, 1, 64, 640, 1 * 10 * 4 * 4096),
     (L.SA_OP_DECODE, 8, 64, 641, 8 * 11 * 4 * 4096),
-    (L.SA_OP_DECODE, 63, 64, 1, 63 * 1 * 4 * 4096),
-    (L.SA_OP_PREFILL, 31, 128, 64, 31 * 1 * 8 * 4096),
+    (L.SA_OP_DECODE, 23, 64, 1, 23 * 1 * 4 * 4096),
+    (L.SA_OP_PREFILL, 11, 128, 64, 11 * 1 * 8 * 4096),
     (L.SA_OP_DECODE, 2, 4, 64, 2 * 1 * 1 * 4096),
     (L.SA_OP_DECODE, 2, 17, 1024, 2 * 16 * 2 * 4096),
     # index lists longer than 1,024 entries stay on the persistent kernels

@@ -276,9 +276,9 @@ def test_determinism_and_guards():
 @pytest.mark.parametrize("heads,alias", [(64, False), (32, False), (16, False), (64, True), (16, True)])
 def test_batch_invariance_across_launch_shapes(heads, alias):
     """A row's bits do not depend on how many rows share the launch: B = 300, 200 and 100 run the
-    persistent kernels with different column slice counts (1, 2 and 4 at 64 heads), which split
-    heads and columns differently; B = 8 and 1 run the split path (every 64-key tile scored in its
-    own workgroup, the scores folded in key order), which runs the same arithmetic."""
+    persistent kernels with one or two column slices, which split heads and columns differently;
+    B = 8 and 1 run the split path (every 64-key tile scored in its own workgroup, the scores
+    folded in key order), which runs the same arithmetic."""
     import sparse_attention_attn_amd as sa
     c = w.decode_bf16(seed=61 + heads, batch=300, heads=heads, n_ctx=1024, k=640)
     d = to_device(c, DEV)

@@ -2,7 +2,7 @@
 workgroup, then the softmax and values per head group and column slice) against the persistent
 kernels (sa_attn.hip) and the float64 oracle.
 
-A launch with fewer than 64 rows per block of 64 heads (and index lists of at most 1,024
+A launch with fewer than 24 rows per block of 64 heads (and index lists of at most 1,024
 entries) takes the split path. The same rows padded with empty rows (nsel = 0, which read
 nothing) to 64 per head block take the persistent kernels. Every real row must come out bit
 for bit the same both ways, and within the tolerance of the oracle: the split changes where
@@ -173,15 +173,16 @@ def test_batched_decode_32k():
 
 @pytest.mark.parametrize("alias", [False, True])
 def test_batch_sweep_bits(alias):
-    """One set of rows launched as batches of 1, 2, 8, 33 and 63 (split path) and 64, 100 and 150
-    (persistent kernels): every row's bits are the same in every launch."""
+    """One set of rows launched as batches of 1, 2, 8 and 23 (split path) and 24, 33, 63, 64, 100
+    and 150 (persistent kernels with 8, 4, 2 and 1 column slices): every row's bits are the same in
+    every launch."""
     sa, _ = _lib()
     c = w.decode_bf16(seed=330, batch=150, heads=64, n_ctx=1024, k=640)
     d = to_device(c, DEV)
     vv = d["k"] if alias else d["v"]
-    say(f"batch sweep{' aliased' if alias else ''}: B in 1, 2, 8, 33, 63 | 64, 100, 150")
+    say(f"batch sweep{' aliased' if alias else ''}: B in 1, 2, 8, 23 | 24, 33, 63, 64, 100, 150")
     full = sa.decode(d["q"], d["k"], vv, d["idx"], d["sinks"], c.scale, d["nsel"])
-    for b in (1, 2, 8, 33, 63, 64, 100):
+    for b in (1, 2, 8, 23, 24, 33, 63, 64, 100):
         part = sa.decode(d["q"][:b], d["k"][:b], vv[:b], d["idx"][:b], d["sinks"], c.scale, d["nsel"][:b])
         torch.cuda.synchronize()
         assert torch.equal(part.view(torch.int32), full[:b].view(torch.int32)), f"B={b}"
