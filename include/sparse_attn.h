@@ -131,6 +131,21 @@ int sparse_attn_decode(int dtype, const void *q, const void *k_cache, const void
                        float *out, void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * Decode without a workspace argument, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid allocation).
+ * The same call as sparse_attn_decode, with the same results bit for bit, except that its
+ * workspace is a static device array of the library, SA_NOALLOC_SCRATCH_BYTES per GPU, held
+ * until the process ends. It allocates nothing. Every call on one GPU shares that GPU's
+ * array: calls in flight at once on one GPU race and must not overlap. A call whose
+ * workspace would exceed the array returns SA_ERR_WORKSPACE before anything is enqueued.
+ */
+#define SA_NOALLOC_SCRATCH_BYTES (8u << 20)
+int sparse_attn_decode_noalloc(int dtype, const void *q, const void *k_cache, const void *v_cache,
+                               int64_t n_ctx, const int32_t *idx, const int32_t *nsel, int32_t kmax,
+                               const float *sinks, float scale, int32_t B, int32_t H, int32_t D,
+                               float *out, void *stream);
+
+/*
  * Prefill: T query rows over ONE shared cache (TensorFold pull request 1206,
  * "What changes": a prefill segment runs the 32-head attention for all its rows).
  * Identical to decode except that every row reads the same cache:

@@ -20,7 +20,7 @@ from . import _lib
 from ._lib import SA_BF16, SA_F32, SparseAttnError, load
 
 HEAD_DIM = 512
-__all__ = ["decode", "prefill", "topk", "pad_heads", "unpad_heads", "workspace_bytes", "load",
+__all__ = ["decode", "decode_noalloc", "prefill", "topk", "pad_heads", "unpad_heads", "workspace_bytes", "load",
            "SparseAttnError", "HEAD_DIM"]
 
 
@@ -112,6 +112,38 @@ def prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, idx: 
             out: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None) -> torch.Tensor:
     """sparse_attn_prefill: T rows over one shared cache [N, 512]. Returns float32 [T, H, 512]."""
     return _attn(True, q, k_cache, v_cache, idx, sinks, scale, nsel, out, ws)
+
+
+def decode_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, idx: torch.Tensor,
+                   sinks: torch.Tensor, scale: float, nsel: Optional[torch.Tensor] = None,
+                   out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """sparse_attn_decode_noalloc: decode with the library's static scratch as workspace (no device
+    allocation by the library; pass `out` to allocate nothing at all). Calls that overlap on one GPU
+    race on the scratch."""
+    _need(q.dim() == 3, "q must be [rows, H, D]")
+    rows, H, D = q.shape
+    _on_device(q, "q", k_cache=k_cache, v_cache=v_cache, idx=idx, sinks=sinks, nsel=nsel, out=out)
+    lib = load()
+    code = _dtype_code(q)
+    _need(k_cache.dtype == q.dtype and v_cache.dtype == q.dtype, "q, k_cache and v_cache must share a dtype")
+    _need(k_cache.dim() == 3 and k_cache.shape[0] == rows and k_cache.shape[2] == D and v_cache.shape == k_cache.shape,
+          "decode caches are [B, N, D]")
+    _need(idx.dtype == torch.int32 and idx.dim() == 2 and idx.shape[0] == rows, "idx must be int32 [rows, kmax]")
+    _need(sinks.dtype == torch.float32 and sinks.shape == (H,), "sinks must be float32 [H]")
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("idx", idx), ("sinks", sinks)):
+        _need(t.is_contiguous(), f"{name} must be contiguous")
+    if nsel is not None:
+        _need(nsel.dtype == torch.int32 and nsel.shape == (rows,) and nsel.is_contiguous(),
+              "nsel must be contiguous int32 [rows]")
+    if out is None:
+        out = torch.empty((rows, H, D), dtype=torch.float32, device=q.device)
+    _need(out.dtype == torch.float32 and out.shape == (rows, H, D) and out.is_contiguous(),
+          "out must be contiguous float32 [rows, H, D]")
+    rc = lib.sparse_attn_decode_noalloc(code, _ptr(q), _ptr(k_cache), _ptr(v_cache), k_cache.shape[1], _ptr(idx),
+                                        _ptr(nsel), idx.shape[1], _ptr(sinks), float(scale), rows, H, D, _ptr(out),
+                                        _stream(q))
+    _lib.check(rc, "sparse_attn_decode_noalloc", lib)
+    return out
 
 
 def topk(scores: torch.Tensor, k: int, valid_len: Optional[torch.Tensor] = None,

@@ -16,6 +16,7 @@ SA_F32, SA_BF16 = 0, 1
 SA_OP_DECODE, SA_OP_PREFILL, SA_OP_TOPK = 0, 1, 2
 SA_HEAD_DIM, SA_MAX_HEADS, SA_BF16_MAX_CTX, SA_MAX_KMAX = 512, 128, 4194303, 1 << 24
 SA_ABI_VERSION = 2
+SA_NOALLOC_SCRATCH_BYTES = 8 << 20
 
 _c = ctypes
 _P = _c.c_void_p
@@ -31,6 +32,8 @@ SIGNATURES = {
                                       _P, _P, _SZ, _P]),
     "sparse_attn_prefill": (_c.c_int, [_c.c_int, _P, _P, _P, _I64, _P, _P, _I32, _P, _F, _I32, _I32, _I32,
                                        _P, _P, _SZ, _P]),
+    "sparse_attn_decode_noalloc": (_c.c_int, [_c.c_int, _P, _P, _P, _I64, _P, _P, _I32, _P, _F, _I32, _I32,
+                                              _I32, _P, _P]),
     "sparse_attn_topk": (_c.c_int, [_P, _I64, _I64, _I64, _P, _I32, _P, _P, _P, _SZ, _P]),
     "sparse_attn_pad_heads": (_c.c_int, [_c.c_int, _P, _I64, _I32, _I32, _I32, _P, _P, _P, _P]),
     "sparse_attn_unpad_heads": (_c.c_int, [_P, _I64, _I32, _I32, _I32, _P, _P]),

@@ -116,6 +116,16 @@ int run_attn(int dtype, const void *q, const void *k, const void *v, int64_t n_c
 
 }  // namespace
 
+namespace sa {
+int run_decode(int dtype, const void *q, const void *k_cache, const void *v_cache, int64_t n_ctx, const int32_t *idx,
+               const int32_t *nsel, int32_t kmax, const float *sinks, float scale, int32_t B, int32_t H, int32_t D,
+               float *out, void *ws, size_t ws_bytes, void *stream) {
+    return run_attn(dtype, q, k_cache, v_cache, n_ctx, idx, nsel, kmax, sinks, scale, B, H, D, out, ws, ws_bytes,
+                    stream, false);
+}
+int fail_with(int code, const char *msg) { return fail(code, "%s", msg); }
+}  // namespace sa
+
 extern "C" {
 
 int sparse_attn_abi_version(void) { return SA_ABI_VERSION; }

@@ -76,4 +76,11 @@ hipError_t launch_attn_split(const AttnArgs &a, hipStream_t s);
 // Compute units of the current device, cached per device (256 if the query fails).
 int device_cu_count();
 
+// The validated decode call behind sparse_attn_decode (for the allocation-free variant in
+// sa_noalloc.hip), and a way for that file to set the calling thread's last error.
+int run_decode(int dtype, const void *q, const void *k_cache, const void *v_cache, int64_t n_ctx, const int32_t *idx,
+               const int32_t *nsel, int32_t kmax, const float *sinks, float scale, int32_t B, int32_t H, int32_t D,
+               float *out, void *ws, size_t ws_bytes, void *stream);
+int fail_with(int code, const char *msg);
+
 }  // namespace sa

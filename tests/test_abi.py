@@ -31,6 +31,8 @@ def test_header_constants_match_binding():
         assert m and int(m.group(1)) == getattr(L, name), name
     m = re.search(r"#define\s+SA_MAX_KMAX\s+\(1 << (\d+)\)", text)
     assert m and 1 << int(m.group(1)) == L.SA_MAX_KMAX
+    m = re.search(r"#define\s+SA_NOALLOC_SCRATCH_BYTES\s+\((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == L.SA_NOALLOC_SCRATCH_BYTES
 
 
 def test_every_declared_symbol_is_exported():
@@ -219,6 +221,26 @@ def test_binding_refuses_host_tensors_everywhere(stub_library):
         sa.unpad_heads(torch.zeros(2, 8, 512), 4, out=torch.zeros(2, 4, 512, device="meta"))
     with pytest.raises(ValueError, match="HIP device"):
         sa.unpad_heads(torch.zeros(2, 8, 512), 4)
+
+
+def test_noalloc_scratch_covers_every_split_launch():
+    """The allocation-free decode's static scratch holds the workspace of every launch that takes
+    the split path (at most 1,024 indices per row, fewer than 24 rows per block of 64 heads)."""
+    lib = L.load()
+    worst = max(lib.sparse_attn_workspace_bytes(L.SA_OP_DECODE, rows, heads, 512, 1024, 4096)
+                for heads in range(1, L.SA_MAX_HEADS + 1) for rows in range(1, 64))
+    assert 0 < worst <= L.SA_NOALLOC_SCRATCH_BYTES
+
+
+def test_noalloc_validation():
+    lib = L.load()
+    args = [L.SA_BF16, A16, A16, A16, 4096, A16, None, 640, A16, 0.04, 1024, 64, 512, A16, None]
+    bad = list(args); bad[12] = 256
+    assert lib.sparse_attn_decode_noalloc(*bad) == L.SA_ERR_UNSUPPORTED
+    bad = list(args); bad[1] = None
+    assert lib.sparse_attn_decode_noalloc(*bad) == L.SA_ERR_NULL
+    bad = list(args); bad[7] = 0
+    assert lib.sparse_attn_decode_noalloc(*bad) == L.SA_ERR_SHAPE
 
 
 def test_zero_rows_is_a_noop_with_null_arrays():
