@@ -242,6 +242,11 @@ attn_bf16_kernel(AttnArgs a, int n_hg, int64_t units) {
     __shared__ int idx_lds[kWaves][2][64];   // each wave's own copy of a tile's index list
     __shared__ float meta_lds[kWaves][3][16];
     __shared__ uint32_t pf_lds[kWaves][64];  // where the L2 prefetches land (never read)
+    // With fewer than four 16-head groups the waves of a key half share heads: each of the two
+    // 16-slot blocks of a group's score tile is computed by one wave and handed to the others
+    // here, [key half][head group][block], instead of every wave computing the whole tile.
+    constexpr bool kShareScores = HQ < 4;
+    __shared__ f32x4 xs_lds[kShareScores ? 2 * HQ * 2 : 1][64];
 
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -252,6 +257,11 @@ attn_bf16_kernel(AttnArgs a, int n_hg, int64_t units) {
     const int cq = wi / HQ;
     const int kh = w >> 2;
     const Stream<NS> str{a, n_hg, units, (int64_t)gridDim.x};
+    // The score block this wave computes, or -1. 32 heads: each of the two waves of a head
+    // group (column parts 0, 1) takes one block. 16 heads: in key half 0 the waves of column
+    // parts 0 and 1 take blocks 0 and 1, in half 1 those of parts 2 and 3, so that every SIMD
+    // (which holds one wave of each half with the same wi) runs one block.
+    const int sblock = HQ == 2 ? cq : (HQ == 1 ? (kh == 0 ? (cq < 2 ? cq : -1) : (cq >= 2 ? cq - 2 : -1)) : 0);
 
     // Wave w gathers tile keys 8w .. 8w+7 (all in its own key half) into both buffers: key
     // 32kh + kap goes to K slot 32kh + kslot_of_key(kap) and to V slot 32kh + swap23(kap).
@@ -342,9 +352,25 @@ attn_bf16_kernel(AttnArgs a, int n_hg, int64_t units) {
             // The tile's V rows go out in the score steps, one every two, in the matrix pipe's
             // shadow (every wave finished the previous tile's values before the barrier).
             const __amdgpu_buffer_rsrc_t rv = rsrc_v(cur);
-            score_chain(krow, qreg, sacc0, sacc1, [&](int kk) {
+            auto hook = [&](int kk) {
                 if (kk % 2 == 0) dma_v_row(rv, iv_cur, kk / 2);
-            });
+            };
+            if constexpr (kShareScores) {
+                f32x4 *xs = xs_lds[(kh * HQ + hq) * 2];
+                if (sblock >= 0) {
+                    f32x4 sb;
+                    score_block_chain(krow + sblock * 16 * kKStride, qreg, sb, hook);
+                    xs[sblock * 64 + lane] = sb;
+                } else {
+#pragma unroll
+                    for (int kk = 0; kk < 16; kk++) hook(kk);
+                }
+                lds_barrier();  // both blocks of every head group's score tile are in LDS
+                sacc0 = xs[lane];
+                sacc1 = xs[64 + lane];
+            } else {
+                score_chain(krow, qreg, sacc0, sacc1, hook);
+            }
         }
 
         // Indices of item j+1 have landed (after them: [stores], V(j)).
@@ -444,6 +470,10 @@ attn_bf16_alias_kernel(AttnArgs a, int n_hg, int64_t units) {
     __shared__ __attribute__((aligned(1024))) char t_lds[2 * kTileBytes];
     __shared__ int idx_lds[kWaves][2][64];
     __shared__ float meta_lds[kWaves][3][16];
+    // Score blocks shared between the waves of a key half that hold the same heads (fewer than
+    // four 16-head groups), as in the separate-cache kernel: [key half][head group][block].
+    constexpr bool kShareScores = HQ < 4;
+    __shared__ f32x4 xs_lds[kShareScores ? 2 * HQ * 2 : 1][64];
 
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -455,6 +485,7 @@ attn_bf16_alias_kernel(AttnArgs a, int n_hg, int64_t units) {
     const int kh = w >> 2;
     const Stream<NS> str{a, n_hg, units, (int64_t)gridDim.x};
     const uint32_t t_base = lds_addr((SA_LDS char *)t_lds);
+    const int sblock = HQ == 2 ? cq : (HQ == 1 ? (kh == 0 ? (cq < 2 ? cq : -1) : (cq >= 2 ? cq - 2 : -1)) : 0);
 
     auto rsrc_t = [&](const Item &it) {
         if (it.unit < 0) return __builtin_amdgcn_make_buffer_rsrc((void *)a.k, 0, 0, kBufferFlags);
@@ -543,7 +574,7 @@ attn_bf16_alias_kernel(AttnArgs a, int n_hg, int64_t units) {
         const __amdgpu_buffer_rsrc_t rt = rsrc_t(nx);
         // ---- scores of the wave's 32 keys for its 16 heads over the full head width.
         f32x4 sacc0 = (f32x4){}, sacc1 = (f32x4){};
-        {
+        if (!kShareScores) {
             const uint32_t kb = tb + kbase;
             bf16x8 k0 = *lds_at<bf16x8>(kb);
             bf16x8 k1 = *lds_at<bf16x8>(kb + 16 * kRowBytes);
@@ -562,6 +593,32 @@ attn_bf16_alias_kernel(AttnArgs a, int n_hg, int64_t units) {
                 k0 = n0;
                 k1 = n1;
             }
+        } else {
+            // One block of the head group's score tile per computing wave (block b's chain: the
+            // same operands in the same order), handed to the other waves through LDS.
+            f32x4 *xs = xs_lds[(kh * HQ + hq) * 2];
+            if (sblock >= 0) {
+                const uint32_t kb = tb + kbase + (uint32_t)(sblock * 16 * kRowBytes);
+                f32x4 sb = (f32x4){};
+                bf16x8 k0 = *lds_at<bf16x8>(kb);
+#pragma unroll
+                for (int kk = 0; kk < 16; kk++) {
+                    bf16x8 n0 = k0;
+                    if (kk + 1 < 16) n0 = *lds_at<bf16x8>(kb ^ (64u * (kk + 1)));
+                    sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qreg[kk], sb, 0, 0, 0);
+                    if (more && kk % 4 == 0) dma_t_row(rt, iv_next, buf ^ 1, kk / 4);
+                    __builtin_amdgcn_sched_barrier(0);
+                    k0 = n0;
+                }
+                xs[sblock * 64 + lane] = sb;
+            } else {
+#pragma unroll
+                for (int kk = 0; kk < 16; kk += 4)
+                    if (more) dma_t_row(rt, iv_next, buf ^ 1, kk / 4);
+            }
+            lds_barrier();  // both blocks of every head group's score tile are in LDS
+            sacc0 = xs[lane];
+            sacc1 = xs[64 + lane];
         }
         // The scores were the last use of qreg in this unit.
         if (q_now) load_q_async(a, nx.row, nx.hg * 16 * HQ + 16 * hq, g, l16, qreg, sink_n);

@@ -256,5 +256,24 @@ __device__ __forceinline__ void score_chain(const SA_LDS char *krow, const bf16x
     }
 }
 
+// One 16-slot block of score_chain on its own: block b's MFMA chain, the same operands in the
+// same order (kblk = krow + 16 b kKStride), for kernels that give the two blocks of a score tile
+// to two waves.
+template <typename Hook>
+__device__ __forceinline__ void score_block_chain(const SA_LDS char *kblk, const bf16x8 (&qreg)[16], f32x4 &sacc,
+                                                  Hook &&hook) {
+    sacc = (f32x4){};
+    bf16x8 k0 = *(const SA_LDS bf16x8 *)(kblk);
+#pragma unroll
+    for (int kk = 0; kk < 16; kk++) {
+        bf16x8 n0 = k0;
+        if (kk + 1 < 16) n0 = *(const SA_LDS bf16x8 *)(kblk + 64 * (kk + 1));
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qreg[kk], sacc, 0, 0, 0);
+        hook(kk);
+        __builtin_amdgcn_sched_barrier(0);
+        k0 = n0;
+    }
+}
+
 }  // namespace
 }  // namespace sa

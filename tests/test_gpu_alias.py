@@ -50,6 +50,8 @@ def alias_and_separate(case):
     (5, 16, 130),      # one head block, 16 real heads of 32
     (40, 32, 65),      # ragged tail tile
     (260, 48, 640),    # two head blocks, the second part-filled
+    (60, 16, 640),     # persistent kernels, one 16-head group: score blocks shared by the waves
+    (30, 32, 130),     # persistent kernels, two 16-head groups: the same
 ])
 def test_alias_bits_equal_separate_and_oracle(batch, heads, k):
     case = aliased(w.decode_bf16(seed=80 + batch + heads, batch=batch, heads=heads,
