@@ -28,6 +28,9 @@ is the decode step above):
                  workgroup; its waves split the output columns four ways)
   prefill-pad16  the same 16 heads copied into a zero-padded 32-head buffer with
                  zero sinks, launched at 32 heads, real heads copied out
+  gather-ceiling the decode workload's K and V row gathers alone, no compute
+                 (sparse_attn_gather_probe): the measured ceiling for this access
+                 pattern, which the decode line also reports next to the HBM peak
 """
 from __future__ import annotations
 
@@ -127,6 +130,47 @@ def cpu_baseline(inp, scores, out_gpu, idx_gpu, heads, k, budget_s: float, max_r
     return base, parity
 
 
+def gather_ceiling(torch, sa, sets, rows: int, k: int, reps: int):
+    """Time sparse_attn_gather_probe (the decode kernels' K and V gathers alone) over the given
+    (inputs, idx) sets with HIP events on the current stream; returns the faster of 8 and 16 rows
+    in flight per wave. Bytes per launch: the gathered bf16 K and V rows and the index list."""
+    nbytes = rows * k * (2 * 2 * 512 + 4)
+    best = None
+    for rif in (8, 16):
+        for i in range(10):
+            inp, idx = sets[i % len(sets)]
+            sa.gather_probe(inp["k"], inp["v"], idx, rif)
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for i in range(reps):
+            inp, idx = sets[i % len(sets)]
+            ev[i][0].record()
+            sa.gather_probe(inp["k"], inp["v"], idx, rif)
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        ms = sum(a.elapsed_time(b) for a, b in ev) / reps
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        if best is None or gbs > best["gbs"]:
+            best = {"gbs": gbs, "frac_of_hbm_peak": gbs / HBM_PEAK_GBS, "rows_in_flight": rif, "kernel_ms": ms,
+                    "bytes_per_launch": nbytes, "kernel": f"gather_probe_kernel<{rif}> (sparse_attn_gather_probe)"}
+    return best
+
+
+def bench_gather_ceiling(args, torch, sa, w, dev) -> int:
+    """The gather probe alone over the decode workload's inputs (one JSON line)."""
+    B, H, N, K = args.batch, args.heads, args.n_ctx, args.k
+    sets = [(w.device_decode_inputs(torch, dev, B, H, N, K, seed=args.seed + i), None) for i in range(2)]
+    sets = [(inp, inp["idx"]) for inp, _ in sets]
+    torch.cuda.synchronize()
+    c = gather_ceiling(torch, sa, sets, B, K, reps=args.steps)
+    print(json.dumps({"metric": "gathered K and V rows, GB/s (no compute)", "value": c["gbs"], "unit": "GB/s",
+                      "n_gpus": 1, "steps": args.steps, "higher_is_better": True, "data": "synthetic",
+                      "config": {"workload": f"gather probe: {B} sequences x {K} selected 1 KiB rows of K and of V "
+                                             f"from {N}-position caches", "batch_rows": B, "n_ctx": N, "k": K},
+                      "gather_ceiling": c}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -143,7 +187,7 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--attn-only", action="store_true", help="time only the attention kernel (profiling)")
     ap.add_argument("--workload", default="decode",
-                    choices=["decode", "decode-alias", "prefill", "prefill-h16", "prefill-pad16"])
+                    choices=["decode", "decode-alias", "prefill", "prefill-h16", "prefill-pad16", "gather-ceiling"])
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB, --steps times "
                          "(calibrates the HBM byte counters against a known size)")
@@ -177,6 +221,8 @@ def main() -> int:
     sa.load()
     if args.workload.startswith("prefill"):
         return bench_prefill(args, torch, sa, w, dev)
+    if args.workload == "gather-ceiling":
+        return bench_gather_ceiling(args, torch, sa, w, dev)
     B, H, N, K = args.batch, args.heads, args.n_ctx, args.k
     alias = args.workload == "decode-alias"
 
@@ -232,6 +278,16 @@ def main() -> int:
         f"algorithmic ({achieved_gbs / HBM_PEAK_GBS:.1%} of 8 TB/s), "
         f"{flops / (attn_ms * 1e-3) / 1e12:.0f} TFLOP/s bf16 ({flops / (attn_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS:.1%} of MFMA peak)")
 
+    # The gather ceiling: the same index-driven K and V row gathers with no compute
+    # (sparse_attn_gather_probe), timed live over the same two input sets, with 8 and 16 rows in
+    # flight per wave; the faster one is the ceiling the attention kernel is compared with.
+    ceiling = None
+    if not alias:
+        ceiling = gather_ceiling(torch, sa, [(st[0], st[2] if not args.attn_only else st[0]["idx"]) for st in sets],
+                                 B, K, reps=max(20, args.steps // 2))
+        log(f"[bench] gather ceiling {ceiling['gbs']:.0f} GB/s ({ceiling['rows_in_flight']} rows in flight per wave, "
+            f"{ceiling['kernel_ms'] * 1e3:.1f} us per launch): attention at {achieved_gbs / ceiling['gbs']:.1%} of it")
+
     inp, scores, idx, cnt, out = sets[(args.steps - 1) % 2]  # the last timed step's set
     result = {
         "metric": "decode query-rows*heads/s (64 heads, d=512, k=640)",
@@ -266,6 +322,8 @@ def main() -> int:
             "kernel_ms": attn_ms,
             "algorithmic_bytes_per_launch": nbytes,
             "mfma_tflops": flops / (attn_ms * 1e-3) / 1e12,
+            "gather_ceiling": ceiling,
+            "frac_of_gather_ceiling": None if ceiling is None else achieved_gbs / ceiling["gbs"],
         },
         "cpu_baseline": None,
     }

@@ -194,6 +194,18 @@ int sparse_attn_pad_heads(int dtype, const void *q, int64_t rows, int32_t h_real
 int sparse_attn_unpad_heads(const float *out_pad, int64_t rows, int32_t h_pad, int32_t h_real,
                             int32_t D, float *out, void *stream);
 
+/*
+ * Measurement only (not part of the method): the decode kernels' gathers alone. For each of
+ * `rows` sequences with caches k_cache / v_cache [rows, n_ctx, 512] bf16, reads the K and V
+ * rows that idx [rows, kmax] selects (an index outside [0, n_ctx) reads nothing) with the same
+ * direct-to-LDS DMAs as sparse_attn_decode, rows_in_flight (8 or 16) of each per wave, and
+ * discards them. Its duration over a batch is the most the decode kernels could reach for that
+ * access pattern; benchmarks report the decode rate against it next to the HBM peak.
+ */
+int sparse_attn_gather_probe(const void *k_cache, const void *v_cache, int64_t n_ctx,
+                             const int32_t *idx, int32_t rows, int32_t kmax, int32_t rows_in_flight,
+                             void *stream);
+
 #ifdef __cplusplus
 }
 #endif

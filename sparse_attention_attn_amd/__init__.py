@@ -209,5 +209,19 @@ def unpad_heads(out_pad: torch.Tensor, h_real: int, out: Optional[torch.Tensor] 
     return out
 
 
+def gather_probe(k_cache: torch.Tensor, v_cache: torch.Tensor, idx: torch.Tensor, rows_in_flight: int = 16) -> None:
+    """sparse_attn_gather_probe: the decode kernels' gathers alone (a bandwidth reference for benchmarks)."""
+    _on_device(k_cache, "k_cache", v_cache=v_cache, idx=idx)
+    lib = load()
+    _need(k_cache.dtype == torch.bfloat16 and k_cache.dim() == 3 and k_cache.shape[2] == HEAD_DIM
+          and v_cache.shape == k_cache.shape and v_cache.dtype == k_cache.dtype
+          and k_cache.is_contiguous() and v_cache.is_contiguous(), "caches must be contiguous bf16 [B, N, 512]")
+    _need(idx.dtype == torch.int32 and idx.dim() == 2 and idx.shape[0] == k_cache.shape[0] and idx.is_contiguous(),
+          "idx must be contiguous int32 [B, kmax]")
+    rc = lib.sparse_attn_gather_probe(_ptr(k_cache), _ptr(v_cache), k_cache.shape[1], _ptr(idx), idx.shape[0],
+                                      idx.shape[1], int(rows_in_flight), _stream(k_cache))
+    _lib.check(rc, "sparse_attn_gather_probe", lib)
+
+
 def workspace_bytes(op: int, rows: int, heads: int, kmax: int, n_ctx: int) -> int:
     return int(load().sparse_attn_workspace_bytes(op, rows, heads, HEAD_DIM, kmax, n_ctx))

@@ -35,6 +35,7 @@ SIGNATURES = {
     "sparse_attn_decode_noalloc": (_c.c_int, [_c.c_int, _P, _P, _P, _I64, _P, _P, _I32, _P, _F, _I32, _I32,
                                               _I32, _P, _P]),
     "sparse_attn_topk": (_c.c_int, [_P, _I64, _I64, _I64, _P, _I32, _P, _P, _P, _SZ, _P]),
+    "sparse_attn_gather_probe": (_c.c_int, [_P, _P, _I64, _P, _I32, _I32, _I32, _P]),
     "sparse_attn_pad_heads": (_c.c_int, [_c.c_int, _P, _I64, _I32, _I32, _I32, _P, _P, _P, _P]),
     "sparse_attn_unpad_heads": (_c.c_int, [_P, _I64, _I32, _I32, _I32, _P, _P]),
 }

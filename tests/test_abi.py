@@ -243,6 +243,16 @@ def test_noalloc_validation():
     assert lib.sparse_attn_decode_noalloc(*bad) == L.SA_ERR_SHAPE
 
 
+def test_gather_probe_validation():
+    lib = L.load()
+    ok = [A16, A16, 4096, A16, 8, 640, 16, None]
+    for i, val, code in [(0, None, L.SA_ERR_NULL), (3, None, L.SA_ERR_NULL), (6, 4, L.SA_ERR_UNSUPPORTED),
+                         (5, 0, L.SA_ERR_SHAPE), (2, 0, L.SA_ERR_SHAPE), (4, -1, L.SA_ERR_SHAPE)]:
+        bad = list(ok); bad[i] = val
+        assert lib.sparse_attn_gather_probe(*bad) == code, (i, val)
+    assert lib.sparse_attn_gather_probe(None, None, 4096, None, 0, 640, 8, None) == L.SA_OK
+
+
 def test_zero_rows_is_a_noop_with_null_arrays():
     lib = L.load()
     assert _decode(lib, q=None, k=None, v=None, idx=None, out=None, rows=0) == L.SA_OK
