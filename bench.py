@@ -28,6 +28,8 @@ is the decode step above):
                  workgroup; its waves split the output columns four ways)
   prefill-pad16  the same 16 heads copied into a zero-padded 32-head buffer with
                  zero sinks, launched at 32 heads, real heads copied out
+  decode-f32     float32 storage, the batched-decode shape (8 sequences x 32,768
+                 positions, k = 640): top-k, then attention on the float32 matrix cores
   gather-ceiling the decode workload's K and V row gathers alone, no compute
                  (sparse_attn_gather_probe): the measured ceiling for this access
                  pattern, which the decode line also reports next to the HBM peak
@@ -156,6 +158,78 @@ def gather_ceiling(torch, sa, sets, rows: int, k: int, reps: int):
     return best
 
 
+MFMA_F32_PEAK_TFLOPS = 157.3
+
+
+def bench_decode_f32(args, torch, sa, w, dev) -> int:
+    """Float32 decode step, batched-decode shape (8 sequences x 32,768 positions unless --batch /
+    --n-ctx say otherwise): top-k over each row's scores, then float32 attention on the matrix
+    cores. Roofline: float32 MFMA peak (the intensity, 32 FLOP/B at 64 heads, is above the float32
+    ridge), with the HBM rate of the algorithmic bytes alongside."""
+    B = args.batch if "--batch" in sys.argv else 8
+    N = args.n_ctx if "--n-ctx" in sys.argv else 32768
+    H, K, D = args.heads, args.k, w.D
+    log(f"[bench] float32 decode: {B} sequences x {N} positions, {H} heads, k = {K}")
+    sets = []
+    for i in range(2):
+        g = torch.Generator(device=dev)
+        g.manual_seed(args.seed + 300 + i)
+        st = {"q": torch.randn((B, H, D), generator=g, device=dev),
+              "k": torch.randn((B, N, D), generator=g, device=dev),
+              "v": torch.randn((B, N, D), generator=g, device=dev),
+              "sinks": torch.randn((H,), generator=g, device=dev),
+              "scores": torch.randn((B, N), generator=g, device=dev),
+              "idx": torch.empty((B, K), dtype=torch.int32, device=dev),
+              "cnt": torch.empty((B,), dtype=torch.int32, device=dev),
+              "out": torch.empty((B, H, D), dtype=torch.float32, device=dev)}
+        sets.append(st)
+    torch.cuda.synchronize()
+
+    def step(i, ev=None):
+        st = sets[i % 2]
+        sa.topk(st["scores"], K, idx_out=st["idx"], count_out=st["cnt"])
+        if ev is not None:
+            ev[0].record()
+        sa.decode(st["q"], st["k"], st["v"], st["idx"], st["sinks"], w.SCALE, out=st["out"])
+        if ev is not None:
+            ev[1].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    events = {i: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for i in range(0, args.steps, EVENT_EVERY)}
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, events.get(i))
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    attn_ms = sum(a.elapsed_time(b) for a, b in events.values()) / len(events)
+    flops = algorithmic_flops(B, H, D, K)
+    nbytes = B * (4 * H * D + 2 * 4 * D * K + 4 * K + 4 * H * D) + 4 * H
+    tflops = flops / (attn_ms * 1e-3) / 1e12
+    gbs = nbytes / (attn_ms * 1e-3) / 1e9
+    log(f"[bench] step {ms_per_step:.3f} ms, attention {attn_ms * 1e3:.1f} us: {tflops:.1f} TFLOP/s float32 "
+        f"({tflops / MFMA_F32_PEAK_TFLOPS:.1%} of the float32 MFMA peak), {gbs:.0f} GB/s ({gbs / HBM_PEAK_GBS:.1%} of HBM)")
+    result = {
+        "metric": f"float32 decode query-rows*heads/s ({H} heads, d=512, k={K})",
+        "value": B * H / (ms_per_step * 1e-3), "unit": "query-rows*heads/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic (seeded, generated on the device)",
+        "config": {"workload": f"float32 decode: {B} sequences x {N} positions, indexer top-{K}, then attention "
+                               f"with per-head sinks at {H} heads on the float32 matrix cores",
+                   "batch_rows": B, "heads": H, "head_dim": D, "n_ctx": N, "k": K},
+        "roofline": {"bound": "mfma", "achieved": tflops, "peak": MFMA_F32_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tflops / MFMA_F32_PEAK_TFLOPS, "traffic": None,
+                     "kernel": "attn_f32_kernel (sparse_attn_decode, SA_F32)", "kernel_ms": attn_ms,
+                     "algorithmic_flops_per_launch": flops, "algorithmic_bytes_per_launch": nbytes,
+                     "hbm_gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def bench_gather_ceiling(args, torch, sa, w, dev) -> int:
     """The gather probe alone over the decode workload's inputs (one JSON line)."""
     B, H, N, K = args.batch, args.heads, args.n_ctx, args.k
@@ -187,7 +261,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--attn-only", action="store_true", help="time only the attention kernel (profiling)")
     ap.add_argument("--workload", default="decode",
-                    choices=["decode", "decode-alias", "prefill", "prefill-h16", "prefill-pad16", "gather-ceiling"])
+                    choices=["decode", "decode-alias", "decode-f32", "prefill", "prefill-h16", "prefill-pad16",
+                             "gather-ceiling"])
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB, --steps times "
                          "(calibrates the HBM byte counters against a known size)")
@@ -223,6 +298,8 @@ def main() -> int:
         return bench_prefill(args, torch, sa, w, dev)
     if args.workload == "gather-ceiling":
         return bench_gather_ceiling(args, torch, sa, w, dev)
+    if args.workload == "decode-f32":
+        return bench_decode_f32(args, torch, sa, w, dev)
     B, H, N, K = args.batch, args.heads, args.n_ctx, args.k
     alias = args.workload == "decode-alias"
 

@@ -77,6 +77,8 @@ extern "C" {
 /* Largest n_ctx (cache positions) of a bf16 call: 4 GiB of cache per 1 KiB position row.
    Larger bf16 caches are refused with SA_ERR_UNSUPPORTED. */
 #define SA_BF16_MAX_CTX 4194303
+/* Largest n_ctx of a float32 call (2 KiB per position row). */
+#define SA_F32_MAX_CTX 2097151
 
 /* Returns SA_ABI_VERSION of the loaded library. */
 int sparse_attn_abi_version(void);
@@ -123,7 +125,7 @@ size_t sparse_attn_workspace_bytes(int op, int64_t rows, int32_t heads, int32_t 
  *   ws        device workspace of ws_bytes >= sparse_attn_workspace_bytes(SA_OP_DECODE, B, H,
  *             D, kmax, n_ctx) bytes (SA_ERR_WORKSPACE if smaller); NULL when that is 0
  * Requires D == 512, 1 <= H <= 128, B >= 0, 1 <= kmax <= SA_MAX_KMAX, n_ctx >= 1
- * (n_ctx <= SA_BF16_MAX_CTX for SA_BF16).
+ * (n_ctx <= SA_BF16_MAX_CTX for SA_BF16, <= SA_F32_MAX_CTX for SA_F32).
  */
 int sparse_attn_decode(int dtype, const void *q, const void *k_cache, const void *v_cache,
                        int64_t n_ctx, const int32_t *idx, const int32_t *nsel, int32_t kmax,

@@ -15,6 +15,7 @@ SA_OK, SA_ERR_NULL, SA_ERR_SHAPE, SA_ERR_UNSUPPORTED, SA_ERR_WORKSPACE, SA_ERR_H
 SA_F32, SA_BF16 = 0, 1
 SA_OP_DECODE, SA_OP_PREFILL, SA_OP_TOPK = 0, 1, 2
 SA_HEAD_DIM, SA_MAX_HEADS, SA_BF16_MAX_CTX, SA_MAX_KMAX = 512, 128, 4194303, 1 << 24
+SA_F32_MAX_CTX = 2097151
 SA_ABI_VERSION = 2
 SA_NOALLOC_SCRATCH_BYTES = 8 << 20
 

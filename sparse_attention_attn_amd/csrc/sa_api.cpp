@@ -78,8 +78,11 @@ int check_attn(int dtype, const void *q, const void *k, const void *v, int64_t n
         const sa::AttnPlan p = sa::plan_attn_bf16(rows, H, kmax);
         if (p.units > kMaxGrid) return fail(SA_ERR_SHAPE, "too many rows for one launch");
         need = p.ws_bytes;
-    } else if ((int64_t)rows * H > kMaxGrid) {
-        return fail(SA_ERR_SHAPE, "too many rows for one launch");
+    } else {
+        if (n_ctx > SA_F32_MAX_CTX)
+            return fail(SA_ERR_UNSUPPORTED, "n_ctx %lld: float32 caches hold at most %d positions", (long long)n_ctx,
+                        SA_F32_MAX_CTX);
+        if ((int64_t)rows * ((H + 15) / 16) > kMaxGrid) return fail(SA_ERR_SHAPE, "too many rows for one launch");
     }
     (void)shared;
     if (ws_bytes < need) return fail(SA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);

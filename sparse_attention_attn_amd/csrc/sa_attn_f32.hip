@@ -1,111 +1,256 @@
-// sa_attn_f32.hip -- gathered sparse attention with per-head sinks for float32 inputs.
+// sa_attn_f32.hip -- gathered sparse attention with per-head sinks for float32 inputs, on the
+// float32 matrix cores (v_mfma_f32_16x16x4_f32).
 //
-// Same definition and the same 64-key online-softmax order as the bf16 kernel
-// (akol1/TensorFold pull request 4, first commit message: 64-key tiles, running
-// maximum, tile sum, value sum; TensorFold pull request 1206, "What changes": a
-// sink per head), computed entirely in float32 with no rounding of the
-// probabilities. This is the precision path for float32 caches; the dense
-// bf16 contractions of the throughput path are in sa_attn.hip.
+// What it computes: akol1/TensorFold pull request 4 ("DeepSeek V4.1: sparse attention on eight
+// SIMD groups, the same bytes"), first commit message: the selected keys are scored in tiles
+// against a 512-wide head, with a running maximum, a tile sum and a value sum in a fixed order;
+// TensorFold pull request 1206, "What changes": a sink logit per head. Everything stays in float32
+// (the weights are never rounded to a narrower type), which is what the 1e-5 bound on float32
+// inputs needs.
 //
-// One workgroup (four waves) serves one (row, head). Per tile: the 64 scores are
-// split four ways over the head width (fixed pairwise combine), the tile maximum
-// and tile sum are taken over the 64 scores in key order, and each thread
-// accumulates two output columns over the tile's keys in key order.
+// How it maps to CDNA4. One workgroup serves one query row and one group of 16 heads, so every
+// selected cache row is gathered from HBM once for 16 heads (the key/value latent is shared by
+// all heads), not once per head. A tile is 32 keys (a float32 row is 2 KiB: a 32-row K tile and
+// a 32-row V tile fill 128 KiB of LDS). Eight waves, two per SIMD:
+//   * Scores S^T = K Q^T, 16 keys x 16 heads per block, two blocks per tile: wave w computes block
+//     b = w & 1 over the dimension quarter dq = w >> 1 (32 MFMA steps of 4 dimensions) and leaves
+//     the partial tile in LDS; each wave then sums the four partials in quarter order (one fixed
+//     reduction order). The contraction's k index runs over dimensions 128 g + kk for lane group g
+//     and step kk, so that a lane reads four steps' K operands with one 16-byte LDS read.
+//   * K slots are ordered so that lane group g's four scores of block b are keys g + 16b + 4j
+//     (j < 4): the lane's eight scores are exactly the weights its value MFMA operand needs (the
+//     operand's k index is key 4s + g at step s). No score or weight moves between lanes.
+//   * Every wave computes the tile's online-softmax step for its 16 heads (the same values in all
+//     waves): tile maximum over 32 keys (in-lane, then two lane swaps), m' = max(m, tile max),
+//     reference r = m' (0 if m' = -inf), alpha = exp(m - r), p = exp(s - r), l = alpha l + sum p,
+//     acc = alpha acc + P V. It starts from m = sink, l = exp(sink - r(sink)).
+//   * Values O^T = V^T P^T: wave w owns 64 of the 512 columns (four 16-column blocks), 8 MFMA steps
+//     of 4 keys per block and tile.
+// Tile j+1's K rows are gathered during tile j's softmax and values, tile j's V rows during its
+// scores. Keys past a row's count, and out-of-range indices, gather zeros through the buffer
+// range (an out-of-range index inside the count makes the row NaN).
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
 
+#include "sa_device.h"
 #include "sa_internal.h"
 
 namespace sa {
 namespace {
 
-constexpr int kHeadDim = 512;
-constexpr int kTile = 64;
+constexpr int kT32 = 32;                   // keys per tile
+constexpr int kRowF = kHeadDim * 4;        // bytes of a float32 cache row
+constexpr int kKStrF = kRowF + 16;         // K slot stride: 16 slots of one read on 16 bank groups
+constexpr int kVStrF = kRowF + 64;         // V row stride: the four lane groups' rows on four bank windows
+constexpr int kWavesF = 8;
+static_assert(kT32 * kKStrF + kT32 * kVStrF + kWavesF * 4 * 64 * 4 <= 160 * 1024, "LDS budget");
 
-__global__ void __launch_bounds__(256) attn_f32_kernel(AttnArgs a) {
-    __shared__ float q_lds[kHeadDim];
-    __shared__ float s_lds[kTile];
-    __shared__ int i_lds[kTile];
+// K slot of tile key kap (0..31): key g + 16b + 4j sits in slot 16b + 4g + j.
+__device__ __forceinline__ int kslot32(int kap) {
+    const int b = kap >> 4, r = kap & 15;
+    return 16 * b + 4 * (r & 3) + (r >> 2);
+}
 
-    const int t = threadIdx.x;
-    const int64_t row = blockIdx.x / a.H;
-    const int head = (int)(blockIdx.x % a.H);
-    const float *qrow = (const float *)a.q + ((int64_t)row * a.H + head) * kHeadDim;
-    const float *kc = (const float *)a.k + (int64_t)row * a.cache_stride;
-    const float *vc = (const float *)a.v + (int64_t)row * a.cache_stride;
-    const int32_t *irow = a.idx + (int64_t)row * a.kmax;
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+attn_f32_kernel(AttnArgs a, int n_hg) {
+    __shared__ __attribute__((aligned(16))) char k_lds[kT32 * kKStrF];
+    __shared__ __attribute__((aligned(16))) char v_lds[kT32 * kVStrF];
+    __shared__ f32x4 part_lds[4][2][64];   // [dimension quarter][block][lane]
+    __shared__ int bad_lds[kWavesF];
+
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int g = lane >> 4;
+    const int l16 = lane & 15;
+    const int b_own = w & 1;
+    const int dq = w >> 1;
+    const int64_t row = blockIdx.x / n_hg;
+    const int hg = (int)(blockIdx.x % n_hg);
+    const int head = 16 * hg + l16;
+    const bool head_ok = head < a.H;
+
     int n = a.nsel ? a.nsel[row] : a.kmax;
     n = n < 0 ? 0 : (n > a.kmax ? a.kmax : n);
+    const int ntiles = (n + kT32 - 1) / kT32;
+    const int32_t *irow = a.idx + row * a.kmax;
 
-    q_lds[2 * t] = qrow[2 * t];
-    q_lds[2 * t + 1] = qrow[2 * t + 1];
-
-    const float sink = a.sinks[head];
-    float m_run = sink;
-    float l_run = expf(sink - ((sink == -INFINITY) ? 0.0f : sink));
-    float acc0 = 0.0f, acc1 = 0.0f;
-    int bad = 0;
-
-    for (int t0 = 0; t0 < n; t0 += kTile) {
-        int my_bad = 0;
-        if (t < kTile) {
-            const int p = t0 + t;
-            int iv = -1;
-            if (p < n) {
-                iv = irow[p];
-                if (iv < 0 || (int64_t)iv >= a.n_ctx) { my_bad = 1; iv = -1; }
-            }
-            i_lds[t] = iv;
+    // The query for this wave's dimension quarter: lane (g, l16) holds dims 128 g + 32 dq .. +31
+    // of head 16 hg + l16 (zero for heads past H).
+    float qv[32];
+    {
+        const float *qrow = (const float *)a.q + (row * a.H + (head_ok ? head : 0)) * kHeadDim + 128 * g + 32 * dq;
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            const f32x4 x = head_ok ? *(const f32x4 *)(qrow + 4 * i) : (f32x4){};
+            qv[4 * i] = x[0];
+            qv[4 * i + 1] = x[1];
+            qv[4 * i + 2] = x[2];
+            qv[4 * i + 3] = x[3];
         }
-        bad |= __syncthreads_or(my_bad);
-
-        // Score of key j = t/4 over the quarter c = t%4 of the head width.
-        const int j = t >> 2, c = t & 3;
-        const int iv = i_lds[j];
-        float part = 0.0f;
-        if (iv >= 0) {
-            const float *krow = kc + (int64_t)iv * kHeadDim + 128 * c;
-            for (int d = 0; d < 128; d++) part = fmaf(q_lds[128 * c + d], krow[d], part);
-        }
-        part += __shfl_xor(part, 1);
-        part += __shfl_xor(part, 2);
-        if (c == 0) s_lds[j] = (t0 + j < n) ? part * a.scale : -INFINITY;
-        __syncthreads();
-
-        float mt = -INFINITY;
-        for (int jj = 0; jj < kTile; jj++) mt = fmaxf(mt, s_lds[jj]);
-        const float m_new = fmaxf(m_run, mt);
-        const float ref = (m_new == -INFINITY) ? 0.0f : m_new;
-        const float alpha = expf(m_run - ref);
-        float ltile = 0.0f, v0 = 0.0f, v1 = 0.0f;
-        for (int jj = 0; jj < kTile; jj++) {
-            const int ij = i_lds[jj];
-            if (ij < 0) continue;  // masked key: absent from the sum
-            const float p = expf(s_lds[jj] - ref);
-            ltile += p;
-            const float *vrow = vc + (int64_t)ij * kHeadDim;
-            v0 = fmaf(p, vrow[2 * t], v0);
-            v1 = fmaf(p, vrow[2 * t + 1], v1);
-        }
-        l_run = alpha * l_run + ltile;
-        acc0 = alpha * acc0 + v0;
-        acc1 = alpha * acc1 + v1;
-        m_run = m_new;
-        __syncthreads();
     }
+    const float sink = head_ok ? a.sinks[head] : 0.0f;
 
-    float *orow = a.out + ((int64_t)row * a.H + head) * kHeadDim;
-    orow[2 * t] = bad ? NAN : acc0 / l_run;
-    orow[2 * t + 1] = bad ? NAN : acc1 / l_run;
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)((const char *)a.k + row * a.cache_stride * 4), 0, (int)(uint32_t)(a.n_ctx * kRowF), kBufferFlags);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)((const char *)a.v + row * a.cache_stride * 4), 0, (int)(uint32_t)(a.n_ctx * kRowF), kBufferFlags);
+    // Tile t's index list: lane l holds entry 32 t + (l & 31), loaded asynchronously (the
+    // address clamped to the row) and resolved once an explicit wait covers it: -1 for a masked
+    // or out-of-range entry, which gathers zeros; bad: a live entry is out of range.
+    bool bad = false;
+    auto load_idx = [&](int t, float &raw) {
+        const int p = t * kT32 + (lane & 31);
+        load4_async(raw, irow + (p < a.kmax ? p : a.kmax - 1));
+    };
+    auto resolve = [&](int t, float &raw) {
+        register_ready(raw);
+        const int p = t * kT32 + (lane & 31);
+        const int iv = __float_as_int(raw);
+        const bool live = p < n;
+        const bool inr = iv >= 0 && (int64_t)iv < a.n_ctx;
+        bad = bad || __builtin_amdgcn_ballot_w64(live && !inr) != 0;
+        return (live && inr) ? iv : -1;
+    };
+    // Wave w gathers tile keys 4w .. 4w+3 of K (two 1 KiB DMAs per row) or of V.
+    auto dma_k = [&](int iv) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int kap = 4 * w + i;
+            const uint32_t off = ((uint32_t)__builtin_amdgcn_readlane(iv, kap) << 11) + ((uint32_t)lane << 4);
+            const uint32_t dst = lds_addr((SA_LDS char *)k_lds + kslot32(kap) * kKStrF);
+            dma16_buf(rk, off, dst);
+            dma16_buf(rk, off + 1024u, dst + 1024u);
+        }
+    };
+    auto dma_v = [&](int iv) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int kap = 4 * w + i;
+            const uint32_t off = ((uint32_t)__builtin_amdgcn_readlane(iv, kap) << 11) + ((uint32_t)lane << 4);
+            const uint32_t dst = lds_addr((SA_LDS char *)v_lds + kap * kVStrF);
+            dma16_buf(rv, off, dst);
+            dma16_buf(rv, off + 1024u, dst + 1024u);
+        }
+    };
+
+    // Online-softmax state (per lane: head l16) and the wave's 64 output columns 64 w + 16 cb +
+    // 4 g + 0..3 of head l16.
+    float m = sink;
+    float ref = (sink == -INFINITY) ? 0.0f : sink;
+    float l = expf(sink - ref);
+    f32x4 acc[4] = {};
+
+    float raw_next;
+    int iv_cur = -1;
+    if (ntiles > 0) {
+        load_idx(0, raw_next);
+        wait_vmcnt<0>();
+        iv_cur = resolve(0, raw_next);
+        dma_k(iv_cur);
+    }
+    const float scale = a.scale;
+    // Per-lane LDS read bases. Scores: slot 16 b_own + l16, dims 128 g + 32 dq + 4i (16 bytes).
+    const SA_LDS char *krow = (const SA_LDS char *)k_lds + (16 * b_own + l16) * kKStrF + (128 * g + 32 * dq) * 4;
+    // Values: row (key) 4s + g, column 64 w + 16 cb + l16.
+    const SA_LDS char *vrow = (const SA_LDS char *)v_lds + g * kVStrF + (64 * w + l16) * 4;
+
+    for (int t = 0; t < ntiles; t++) {
+        wait_vmcnt<0>();   // K(t) has landed (the only operations in flight)
+        lds_barrier();     // every wave's K(t) rows have landed; every wave is done with V(t-1)
+        const bool more = t + 1 < ntiles;
+        if (more) load_idx(t + 1, raw_next);  // I(t+1), then V(t) during the scores
+        dma_v(iv_cur);
+        // ---- partial scores of block b_own over the dimension quarter dq
+        f32x4 sp = {};
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            const f32x4 kx = *(const SA_LDS f32x4 *)(krow + 16 * i);
+#pragma unroll
+            for (int e = 0; e < 4; e++)
+                sp = __builtin_amdgcn_mfma_f32_16x16x4f32(kx[e], qv[4 * i + e], sp, 0, 0, 0);
+        }
+        part_lds[dq][b_own][lane] = sp;
+        lds_barrier();     // all partials are in LDS; every wave is done with K(t)
+        int iv_next = -1;
+        if (more) {
+            wait_vmcnt<8>();  // I(t+1) has landed (after it: the eight V(t) gathers)
+            iv_next = resolve(t + 1, raw_next);
+            dma_k(iv_next);   // K(t+1), during the softmax and the values
+        }
+        // ---- scores: the four quarters in order; lane (g, l16): keys g + 4e of the tile
+        float s[8];
+        float mt = -INFINITY;
+#pragma unroll
+        for (int bb = 0; bb < 2; bb++) {
+            const f32x4 p0 = part_lds[0][bb][lane], p1 = part_lds[1][bb][lane];
+            const f32x4 p2 = part_lds[2][bb][lane], p3 = part_lds[3][bb][lane];
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                const int e = 4 * bb + j;
+                const float tot = ((p0[j] + p1[j]) + p2[j]) + p3[j];
+                s[e] = t * kT32 + g + 4 * e < n ? tot * scale : -INFINITY;
+                mt = fmaxf(mt, s[e]);
+            }
+        }
+        mt = max_xor32(max_xor16(mt));
+        const float m_new = fmaxf(m, mt);
+        const float ref_new = (m_new == -INFINITY) ? 0.0f : m_new;
+        const float alpha = expf(m - ref_new);
+        float pe[8];
+        float psum = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; e++) {
+            pe[e] = s[e] == -INFINITY ? 0.0f : expf(s[e] - ref_new);
+            psum += pe[e];
+        }
+        psum = sum_xor32(sum_xor16(psum));
+        l = alpha * l + psum;
+        m = m_new;
+        ref = ref_new;
+#pragma unroll
+        for (int cb = 0; cb < 4; cb++) acc[cb] *= alpha;
+        // ---- values: V(t) has landed (after it only K(t+1) is in flight)
+        if (more) wait_vmcnt<8>(); else wait_vmcnt<0>();
+        lds_barrier();
+#pragma unroll
+        for (int st = 0; st < 8; st++) {
+#pragma unroll
+            for (int cb = 0; cb < 4; cb++) {
+                const float vx = *(const SA_LDS float *)(vrow + 4 * st * kVStrF + 64 * cb);
+                acc[cb] = __builtin_amdgcn_mfma_f32_16x16x4f32(vx, pe[st], acc[cb], 0, 0, 0);
+            }
+        }
+        iv_cur = iv_next;
+    }
+    wait_vmcnt<0>();
+    (void)ref;
+
+    // Whole-row NaN for an out-of-range index (any wave saw one), else acc / l.
+    if (lane == 0) bad_lds[w] = bad;
+    lds_barrier();
+    bool row_bad = false;
+#pragma unroll
+    for (int i = 0; i < kWavesF; i++) row_bad = row_bad || bad_lds[i] != 0;
+    if (head_ok) {
+        float *orow = a.out + (row * a.H + head) * kHeadDim + 64 * w + 4 * g;
+#pragma unroll
+        for (int cb = 0; cb < 4; cb++) {
+            f32x4 o;
+#pragma unroll
+            for (int e = 0; e < 4; e++) o[e] = row_bad ? __uint_as_float(0x7fc00000u) : acc[cb][e] / l;
+            *(f32x4 *)(orow + 16 * cb) = o;
+        }
+    }
 }
 
 }  // namespace
 
 hipError_t launch_attn_f32(const AttnArgs &a, hipStream_t s) {
-    const int64_t grid = (int64_t)a.rows * a.H;
+    const int n_hg = (a.H + 15) / 16;
+    const int64_t grid = (int64_t)a.rows * n_hg;
     if (grid == 0) return hipSuccess;
-    hipLaunchKernelGGL(attn_f32_kernel, dim3((unsigned)grid), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(attn_f32_kernel, dim3((unsigned)grid), dim3(512), 0, s, a, n_hg);
     return hipGetLastError();
 }
 

@@ -26,7 +26,7 @@ def test_header_and_binding_agree():
 
 def test_header_constants_match_binding():
     text = open(HEADER).read()
-    for name in ("SA_HEAD_DIM", "SA_MAX_HEADS", "SA_BF16_MAX_CTX", "SA_ABI_VERSION"):
+    for name in ("SA_HEAD_DIM", "SA_MAX_HEADS", "SA_BF16_MAX_CTX", "SA_F32_MAX_CTX", "SA_ABI_VERSION"):
         m = re.search(r"#define\s+%s\s+(\d+)" % name, text)
         assert m and int(m.group(1)) == getattr(L, name), name
     m = re.search(r"#define\s+SA_MAX_KMAX\s+\(1 << (\d+)\)", text)
@@ -103,6 +103,7 @@ def _decode(lib, **kw):
     (dict(rows=8, ws=A16 + 8, ws_bytes=8 * 10 * 4 * 4096), L.SA_ERR_UNSUPPORTED),
     (dict(n_ctx=0), L.SA_ERR_SHAPE),
     (dict(n_ctx=4194304), L.SA_ERR_UNSUPPORTED),  # bf16 caches: at most 2^22 - 1 positions
+    (dict(dtype=L.SA_F32, n_ctx=2097152), L.SA_ERR_UNSUPPORTED),  # float32 caches: at most 2^21 - 1
     (dict(q=A16 + 8), L.SA_ERR_UNSUPPORTED),
     (dict(out=A16 + 4), L.SA_ERR_UNSUPPORTED),
     (dict(idx=A16 + 2), L.SA_ERR_UNSUPPORTED),

@@ -143,6 +143,18 @@ def decode_bf16(seed: int = 1, batch: int = 1, heads: int = 64, n_ctx: int = 409
     return AttnCase(name, "bf16", q, kc, vc, idx, nsel, sinks, SCALE, False)
 
 
+def decode_f32(seed: int = 6, batch: int = 1, heads: int = 64, n_ctx: int = 4096, k: int = 640,
+               name: str = "decode_f32") -> AttnCase:
+    """Decode with float32 storage: `batch` sequences, each with its own n_ctx-position cache."""
+    rng = np.random.default_rng(seed)
+    q = _normal(rng, (batch, heads, D))
+    kc = _normal(rng, (batch, n_ctx, D))
+    vc = _normal(rng, (batch, n_ctx, D))
+    sinks = rng.standard_normal(heads, dtype=np.float32)
+    idx, nsel = _pack_idx([sorted_unique_indices(rng, n_ctx, min(k, n_ctx)) for _ in range(batch)])
+    return AttnCase(name, "f32", q, kc, vc, idx, nsel, sinks, SCALE, False)
+
+
 def batched_decode_bf16(seed: int = 2, batch: int = 8, heads: int = 64, n_ctx: int = 32768,
                         k: int = 640) -> AttnCase:
     """Batched decode: 8 sequences with 32,768 cached positions each, k = 640 (or an edge k)."""
