@@ -69,7 +69,7 @@ def algorithmic_flops(rows: int, heads: int, d: int, k: int) -> int:
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "attn_decode_b1024_h64_k640_hbm_traffic.md")
 # The attention kernel's sources: the recorded counters apply while their sha256 (of the
 # files' bytes in this order) is unchanged.
-KERNEL_SOURCES = [os.path.join(ROOT, "sparse_attention_attn_amd", "csrc", f) for f in ("sa_attn.hip", "sa_device.h")]
+KERNEL_SOURCES = [os.path.join(ROOT, "sparse_attention_attn_amd", "csrc", f) for f in ("sa_attn.hip", "sa_attn_common.h", "sa_device.h", "sa_internal.h")]
 
 
 def measured_traffic(rows: int, heads: int, n_ctx: int, k: int):
