@@ -69,3 +69,61 @@ def test_captured_step_replays_equal_eager(shared):
         torch.cuda.synchronize()
         assert torch.equal(idx, ref_idx), f"replay {r}: indices differ from eager"
         assert torch.equal(out.view(torch.int32), ref_out.view(torch.int32)), f"replay {r}: outputs differ"
+
+
+@pytest.mark.parametrize("entry", ["decode", "decode_noalloc"])
+def test_captured_split_step_replays_equal_eager(entry):
+    """Three sequences take the split path (score tiles through a workspace, then the values
+    kernel). Captured with a workspace the caller allocated beforehand (sparse_attn_decode) or
+    with the library's static scratch (sparse_attn_decode_noalloc, for callers that cannot
+    allocate under capture); every replay must equal the eager result bit for bit."""
+    import sparse_attention_attn_amd as sa
+    from sparse_attention_attn_amd import _lib as L
+    rows, H, N, K = 3, 64, 2048, 640
+    assert sa.workspace_bytes(L.SA_OP_DECODE, rows, H, K, N) > 0, "not the split path"
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(19)
+
+    def draw():
+        return {
+            "q": torch.randn((rows, H, 512), generator=gen, device=DEV).to(torch.bfloat16),
+            "k": torch.randn((rows, N, 512), generator=gen, device=DEV).to(torch.bfloat16),
+            "v": torch.randn((rows, N, 512), generator=gen, device=DEV).to(torch.bfloat16),
+            "sinks": torch.randn((H,), generator=gen, device=DEV),
+            "scores": torch.randn((rows, N), generator=gen, device=DEV),
+        }
+
+    bufs = draw()
+    idx = torch.empty((rows, K), dtype=torch.int32, device=DEV)
+    cnt = torch.empty((rows,), dtype=torch.int32, device=DEV)
+    out = torch.empty((rows, H, 512), dtype=torch.float32, device=DEV)
+    ws = torch.empty((sa.workspace_bytes(L.SA_OP_DECODE, rows, H, K, N),), dtype=torch.uint8, device=DEV)
+
+    def step():
+        sa.topk(bufs["scores"], K, idx_out=idx, count_out=cnt)
+        if entry == "decode":
+            sa.decode(bufs["q"], bufs["k"], bufs["v"], idx, bufs["sinks"], w.SCALE, cnt, out=out, ws=ws)
+        else:
+            sa.decode_noalloc(bufs["q"], bufs["k"], bufs["v"], idx, bufs["sinks"], w.SCALE, cnt, out=out)
+
+    def eager(inp):
+        i2, c2 = sa.topk(inp["scores"], K)
+        return i2, sa.decode(inp["q"], inp["k"], inp["v"], i2, inp["sinks"], w.SCALE, c2)
+
+    step()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    for r in range(4):
+        say(f"split-path {entry} graph replay {r}")
+        new = draw()
+        for key, t in bufs.items():
+            t.copy_(new[key])
+        ref_idx, ref_out = eager(new)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(idx, ref_idx), f"replay {r}: indices differ from eager"
+        assert torch.equal(out.view(torch.int32), ref_out.view(torch.int32)), f"replay {r}: outputs differ"
