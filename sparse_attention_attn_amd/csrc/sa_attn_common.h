@@ -111,10 +111,13 @@ __device__ __forceinline__ float tile_scores(const f32x4 &s0, const f32x4 &s1, i
 __device__ __forceinline__ bool tile_reference(HalfState &st, float mloc, float &ref_prev) {
 #pragma clang fp contract(off)
     const float m_new = fmaxf(st.m, mloc);
-    const bool move = m_new > st.ref + kLazy || (m_new < st.ref && m_new != -INFINITY);
+    // Bitwise forms and a select: no exec-mask branches in a chain that a wave may walk tile
+    // after tile (the same values as the short-circuit form).
+    const bool move = (m_new > st.ref + kLazy) | ((m_new < st.ref) & (m_new != -INFINITY));
     const bool rescale = __builtin_amdgcn_ballot_w64(move) != 0;
     ref_prev = st.ref;
-    if (rescale) st.ref = (m_new == -INFINITY) ? 0.0f : m_new;
+    const float ref_new = (m_new == -INFINITY) ? 0.0f : m_new;
+    st.ref = rescale ? ref_new : st.ref;
     st.m = m_new;
     return rescale;
 }

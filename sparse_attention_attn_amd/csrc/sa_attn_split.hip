@@ -244,31 +244,41 @@ attn_split_values_kernel(AttnArgs a, int ntiles_max, int n_hg) {
         lds_barrier();  // every wave's slices and score pieces have landed
 
         // Phase 1: scaled scores and the tile maximum of this wave's tiles of the round (qv,
-        // qv + 4, qv + 8); the maxima go to LDS for the reference scan.
+        // qv + 4, qv + 8); the maxima go to LDS for the reference scan. Every LDS read of a phase
+        // goes out before the first use (a slot past the round's tiles is read and not used), so
+        // the reads' latencies overlap instead of adding up tile by tile.
         constexpr int kMine = (kRing + 3) / 4;
         float sk[kMine][8];
+        f32x4 sraw[kMine][2];
+#pragma unroll
+        for (int j = 0; j < kMine; j++) {
+            const int i = qv + 4 * j < kRing ? qv + 4 * j : kRing - 1;
+            const SA_LDS f32x4 *sp = lds_at<f32x4>(s_base + i * kSTileB + (kh * 64 + lane) * 32);
+            sraw[j][0] = sp[0];
+            sraw[j][1] = sp[1];
+        }
 #pragma unroll
         for (int j = 0; j < kMine; j++) {
             const int i = qv + 4 * j;
             if (i < nt) {
                 const int t = t0 + i;
-                const SA_LDS f32x4 *sp = lds_at<f32x4>(s_base + i * kSTileB + (kh * 64 + lane) * 32);
-                const f32x4 s0 = sp[0], s1 = sp[1];
-                mloc_lds[kh][i][lane] =
-                    tile_scores(s0, s1, t * kTile + 32 * kh + 8 * g, n, (t + 1) * kTile <= n, scale2, sk[j]);
+                mloc_lds[kh][i][lane] = tile_scores(sraw[j][0], sraw[j][1], t * kTile + 32 * kh + 8 * g, n,
+                                                    (t + 1) * kTile <= n, scale2, sk[j]);
             }
         }
         lds_barrier();
         // Phase 2: the reference scan over the round's tiles in key order (every wave of a key
         // half computes the same values), then the weights of this wave's tiles against their
         // references, written over their scores.
-        float ref_t[kRing], refp_t[kRing];
+        float ref_t[kRing], refp_t[kRing], mloc_t[kRing];
         uint32_t resc = 0;
+#pragma unroll
+        for (int i = 0; i < kRing; i++) mloc_t[i] = mloc_lds[kh][i][lane];
 #pragma unroll
         for (int i = 0; i < kRing; i++) {
             if (i < nt) {
                 float rp;
-                const bool r = tile_reference(st, mloc_lds[kh][i][lane], rp);
+                const bool r = tile_reference(st, mloc_t[i], rp);
                 ref_t[i] = st.ref;
                 refp_t[i] = rp;
                 resc |= (uint32_t)r << i;
@@ -292,23 +302,35 @@ attn_split_values_kernel(AttnArgs a, int ntiles_max, int n_hg) {
             }
         }
         lds_barrier();
-        // Phase 3: tile sums, rescales and value MFMAs in key order.
+        // Phase 3: tile sums, rescales and value MFMAs in key order. The tile sums are read up
+        // front, and each tile's weights and value operand one tile ahead of its MFMAs.
+        float psum_t[kRing];
+#pragma unroll
+        for (int i = 0; i < kRing; i++) psum_t[i] = psum_lds[kh][i][lane];
+        auto operands = [&](int i, bf16x8 &ph, bf16x8 &pl, bf16x8 &vop) {
+            const SA_LDS bf16x8 *pp = lds_at<bf16x8>(s_base + i * kSTileB + (kh * 64 + lane) * 32);
+            ph = pp[0];
+            pl = pp[1];
+            const uint32_t vt = v_base + i * kVTileB;
+            const bf16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((SA_LDS bf16x4 *)lds_at<bf16x4>(vt + vaddr[0]));
+            const bf16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((SA_LDS bf16x4 *)lds_at<bf16x4>(vt + vaddr[1]));
+            vop = (bf16x8){r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]};
+        };
+        bf16x8 ph_c, pl_c, v_c;
+        operands(0, ph_c, pl_c, v_c);
 #pragma unroll
         for (int i = 0; i < kRing; i++) {
             if (i < nt) {
+                bf16x8 ph_n = ph_c, pl_n = pl_c, v_n = v_c;
+                if (i + 1 < kRing) operands(i + 1, ph_n, pl_n, v_n);
                 const bool r = (resc >> i) & 1u;
                 const float alpha = tile_alpha(r, st.l, refp_t[i], ref_t[i]);
-                tile_accumulate(st, r, alpha, psum_lds[kh][i][lane], acc);
-                const SA_LDS bf16x8 *pp = lds_at<bf16x8>(s_base + i * kSTileB + (kh * 64 + lane) * 32);
-                const bf16x8 ph = pp[0], pl = pp[1];
-                const uint32_t vt = v_base + i * kVTileB;
-                const bf16x4 r0 =
-                    __builtin_amdgcn_ds_read_tr16_b64_v4bf16((SA_LDS bf16x4 *)lds_at<bf16x4>(vt + vaddr[0]));
-                const bf16x4 r1 =
-                    __builtin_amdgcn_ds_read_tr16_b64_v4bf16((SA_LDS bf16x4 *)lds_at<bf16x4>(vt + vaddr[1]));
-                const bf16x8 vop = (bf16x8){r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]};
-                acc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, ph, acc[0], 0, 0, 0);
-                acc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pl, acc[0], 0, 0, 0);
+                tile_accumulate(st, r, alpha, psum_t[i], acc);
+                acc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v_c, ph_c, acc[0], 0, 0, 0);
+                acc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v_c, pl_c, acc[0], 0, 0, 0);
+                ph_c = ph_n;
+                pl_c = pl_n;
+                v_c = v_n;
             }
         }
         lds_barrier();  // every wave is done with this round's buffers
