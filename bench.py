@@ -124,10 +124,23 @@ def cpu_baseline(inp, scores, out_gpu, idx_gpu, heads, k, budget_s: float, max_r
         max_err = max(max_err, float(err.max()) if err.size else 0.0)
         rows_done += 1
     value = rows_done * heads / t_total
+    # The same oracle on one thread, over the first rows again (about 2 s of work).
+    rows_1, t_1 = 0, 0.0
+    while rows_1 < rows_done and t_1 < 2.0:
+        case = w.host_case_from_device(inp, rows_1)
+        s = scores[rows_1:rows_1 + 1].cpu().numpy()
+        t0 = time.perf_counter()
+        idx, cnt = oracle.topk(s, k, lib=lib)
+        oracle.attention(case.dtype, case.q, case.k, case.v, idx, cnt, case.sinks, case.scale, False, threads=1,
+                         lib=lib)
+        t_1 += time.perf_counter() - t0
+        rows_1 += 1
     base = {"value": value, "unit": "query-rows*heads/s", "cores": threads, "kind": "oracle",
             "sample": f"the first {rows_done} of the batch's {max_rows} rows (top-k over the row's scores, "
                       f"then {heads}-head attention), {t_total:.1f} s of float64 oracle work on "
-                      f"{threads} OpenMP threads"}
+                      f"{threads} OpenMP threads",
+            "single_thread": {"value": rows_1 * heads / t_1, "cores": 1,
+                              "sample": f"the first {rows_1} rows again, {t_1:.1f} s on one thread"}}
     parity = {"rows": rows_done, "indices_bit_exact_and_attention_within_tol": ok, "max_abs_err": max_err}
     return base, parity
 
@@ -156,6 +169,27 @@ def gather_ceiling(torch, sa, sets, rows: int, k: int, reps: int):
             best = {"gbs": gbs, "frac_of_hbm_peak": gbs / HBM_PEAK_GBS, "rows_in_flight": rif, "kernel_ms": ms,
                     "bytes_per_launch": nbytes, "kernel": f"gather_probe_kernel<{rif}> (sparse_attn_gather_probe)"}
     return best
+
+
+def copy_peak(torch, dev, mib: int = 1024, reps: int = 10):
+    """A plain device-to-device copy of `mib` MiB (torch's copy kernel), timed with HIP events:
+    bytes read plus bytes written per second, the streaming rate of this part as context for
+    the gather ceiling."""
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del src, dst
+    return {"gbs": 2 * n / (ms * 1e-3) / 1e9, "bytes_moved_per_copy": 2 * n, "kernel_ms": ms}
 
 
 def small_batch_latency(torch, sa, w, dev, n_ctx: int, k: int, heads: int, seed: int):
@@ -393,6 +427,7 @@ def main() -> int:
                 sa.topk(st[1], K, idx_out=st[2], count_out=st[3])
         ceiling = gather_ceiling(torch, sa, [(st[0], st[2] if not args.attn_only else st[0]["idx"]) for st in sets],
                                  B, K, reps=250)
+        ceiling["copy_peak"] = copy_peak(torch, dev)
 
     for i in range(args.warmup):
         step(i)
@@ -421,7 +456,8 @@ def main() -> int:
 
     if ceiling is not None:
         log(f"[bench] gather ceiling {ceiling['gbs']:.0f} GB/s ({ceiling['rows_in_flight']} rows in flight per wave, "
-            f"{ceiling['kernel_ms'] * 1e3:.1f} us per launch): attention at {achieved_gbs / ceiling['gbs']:.1%} of it")
+            f"{ceiling['kernel_ms'] * 1e3:.1f} us per launch): attention at {achieved_gbs / ceiling['gbs']:.1%} of it; "
+            f"a 1 GiB device copy moves {ceiling['copy_peak']['gbs']:.0f} GB/s")
 
     small = None
     if not alias and not args.attn_only and (B, H, N, K) == (1024, 64, 4096, 640):
