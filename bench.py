@@ -67,16 +67,31 @@ def algorithmic_flops(rows: int, heads: int, d: int, k: int) -> int:
 
 
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "attn_decode_b1024_h64_k640_hbm_traffic.md")
-# The attention kernel's sources: the recorded counters apply while their sha256 (of the
-# files' bytes in this order) is unchanged.
+# The attention kernel's sources: the recorded counters apply while the sha256 of their code
+# (kernel_code_sha256) is unchanged.
 KERNEL_SOURCES = [os.path.join(ROOT, "sparse_attention_attn_amd", "csrc", f) for f in ("sa_attn.hip", "sa_attn_common.h", "sa_device.h", "sa_internal.h")]
+
+
+def kernel_code_sha256(files=None) -> str:
+    """sha256 of the code of the given sources (KERNEL_SOURCES by default) in order, with
+    comments, trailing blanks and blank lines removed: a change to a comment keeps the
+    recorded counters, any change to the code does not."""
+    import hashlib
+    import re
+    h = hashlib.sha256()
+    for f in files or KERNEL_SOURCES:
+        text = open(f).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        lines = [ln.rstrip() for ln in text.splitlines() if ln.strip()]
+        h.update(("\n".join(lines) + "\n").encode())
+    return h.hexdigest()
 
 
 def measured_traffic(rows: int, heads: int, n_ctx: int, k: int):
     """HBM bytes per attention launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary
     (copy-calibrated), or None when that summary was taken on another workload or on a kernel
     source that has changed since (its recorded sha256 no longer matches)."""
-    import hashlib
     if (rows, heads, n_ctx, k) != (1024, 64, 4096, 640) or not os.path.exists(TRAFFIC_PROFILE):
         return None
     fields = {}
@@ -84,8 +99,7 @@ def measured_traffic(rows: int, heads: int, n_ctx: int, k: int):
         if ":" in line and not line.startswith(("|", " ", "#")):
             key, val = line.split(":", 1)
             fields[key.strip()] = val.strip()
-    sha = hashlib.sha256(b"".join(open(f, "rb").read() for f in KERNEL_SOURCES)).hexdigest()
-    if fields.get("kernel_source_sha256") != sha or "traffic_bytes_per_launch" not in fields:
+    if fields.get("kernel_code_sha256") != kernel_code_sha256() or "traffic_bytes_per_launch" not in fields:
         return None
     return int(fields["traffic_bytes_per_launch"])
 

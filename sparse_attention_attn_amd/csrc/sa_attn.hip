@@ -29,10 +29,16 @@
 //     gathered buffer from the waves that filled it to the waves that read it, and back.
 //   * Gathers are index-driven direct-to-LDS DMAs through buffer resources (a masked key
 //     reads zeros), issued one row at a time inside the MFMA loops.
-//   * Splitting work across workgroups or waves only ever splits heads and output columns
-//     (each wave's scores are contracted over the whole head width, whatever it stores),
-//     never keys, so results are bit-identical across launch shapes, head counts and
-//     repeats, and the two kernels give the same bits on equal contents.
+//   * With fewer than four 16-head groups per block (HQ < 4), several waves of a key half
+//     hold the same heads; each 16-key block of their score tile is then contracted by one
+//     wave and handed to the others through LDS, so no score is computed twice.
+//   * In these kernels, splitting work across workgroups or waves only ever splits heads and
+//     output columns (every score is contracted over the whole head width in one wave); the
+//     keys of a tile always go to the same two halves. The small-batch path
+//     (sa_attn_split.hip) scores each 64-key tile in its own workgroup with the same score
+//     chain and then runs the same per-tile steps in key order. So results are bit-identical
+//     across launch shapes, head counts, paths and repeats, and the two kernels here give the
+//     same bits on equal contents.
 //
 // Numerics, in log2 units (x2 = x * log2 e), per wave and 32-key half tile: m' = max(m,
 // max_j s_j); the exponent reference r moves to m' (0 if m' = -inf) with alpha = 2^(r - r')
