@@ -104,8 +104,10 @@ const char *sparse_attn_last_error(void);
  * products fold them in key order. Larger batches need no workspace. A row's
  * result is the same, bit for bit, on either path (the ds4 commit log for
  * ds4_tp.c: a split that follows the launch must not change the output bytes).
- * The value depends only on (op, rows, heads, kmax); the float32 path needs none,
- * so this is an upper bound for it.
+ * Float32 launches with fewer than 17 rows per block of 64 heads and index lists
+ * of 129 to 1,024 entries split the same way, with 32-key tiles of 2 KiB (rows x
+ * ceil(kmax / 32) x ceil(heads / 16) x 2 KiB, never more than the bf16 figure).
+ * The value depends only on (op, rows, heads, kmax) and covers both storage types.
  */
 size_t sparse_attn_workspace_bytes(int op, int64_t rows, int32_t heads, int32_t head_dim,
                                    int32_t kmax, int64_t n_ctx);

@@ -83,7 +83,7 @@ def _attn(shared: bool, q, k_cache, v_cache, idx, sinks, scale, nsel, out, ws):
           "out must be contiguous float32 [rows, H, D]")
     kmax = idx.shape[1]
     need = 0
-    if code == SA_BF16 and 1 <= kmax <= _lib.SA_MAX_KMAX:
+    if 1 <= kmax <= _lib.SA_MAX_KMAX:
         need = int(lib.sparse_attn_workspace_bytes(_lib.SA_OP_PREFILL if shared else _lib.SA_OP_DECODE,
                                                    rows, H, D, kmax, n_ctx))
     if ws is None and need > 0:

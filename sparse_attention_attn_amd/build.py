@@ -21,8 +21,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libsparse_attn.so")
-SOURCES = ["sa_api.cpp", "sa_attn.hip", "sa_attn_split.hip", "sa_attn_f32.hip", "sa_topk.hip", "sa_pad.hip",
-           "sa_noalloc.hip", "sa_probe.hip"]
+SOURCES = ["sa_api.cpp", "sa_attn.hip", "sa_attn_split.hip", "sa_attn_f32.hip", "sa_attn_f32_split.hip", "sa_topk.hip",
+           "sa_pad.hip", "sa_noalloc.hip", "sa_probe.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

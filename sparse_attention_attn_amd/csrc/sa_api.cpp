@@ -83,6 +83,7 @@ int check_attn(int dtype, const void *q, const void *k, const void *v, int64_t n
             return fail(SA_ERR_UNSUPPORTED, "n_ctx %lld: float32 caches hold at most %d positions", (long long)n_ctx,
                         SA_F32_MAX_CTX);
         if ((int64_t)rows * ((H + 15) / 16) > kMaxGrid) return fail(SA_ERR_SHAPE, "too many rows for one launch");
+        if (sa::f32_split_applies(rows, H, kmax)) need = sa::f32_split_workspace_bytes(rows, H, kmax);
     }
     (void)shared;
     if (ws_bytes < need) return fail(SA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
@@ -120,6 +121,13 @@ int run_attn(int dtype, const void *q, const void *k, const void *v, int64_t n_c
 }  // namespace
 
 namespace sa {
+int check_decode(int dtype, const void *q, const void *k_cache, const void *v_cache, int64_t n_ctx, const int32_t *idx,
+                 const int32_t *nsel, int32_t kmax, const float *sinks, float scale, int32_t B, int32_t H, int32_t D,
+                 float *out, void *ws, size_t ws_bytes) {
+    const int rc = check_attn(dtype, q, k_cache, v_cache, n_ctx, idx, nsel, kmax, sinks, scale, B, H, D, out, ws,
+                              ws_bytes, false);
+    return rc == SA_OK ? ok() : rc;
+}
 int run_decode(int dtype, const void *q, const void *k_cache, const void *v_cache, int64_t n_ctx, const int32_t *idx,
                const int32_t *nsel, int32_t kmax, const float *sinks, float scale, int32_t B, int32_t H, int32_t D,
                float *out, void *ws, size_t ws_bytes, void *stream) {

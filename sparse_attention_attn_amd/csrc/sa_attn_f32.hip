@@ -33,24 +33,16 @@
 #include <math.h>
 #include <stdint.h>
 
+#include "sa_attn_f32_common.h"
 #include "sa_device.h"
 #include "sa_internal.h"
 
 namespace sa {
 namespace {
 
-constexpr int kT32 = 32;                   // keys per tile
-constexpr int kRowF = kHeadDim * 4;        // bytes of a float32 cache row
-constexpr int kKStrF = kRowF + 16;         // K slot stride: 16 slots of one read on 16 bank groups
 constexpr int kVStrF = kRowF + 64;         // V row stride: the four lane groups' rows on four bank windows
 constexpr int kWavesF = 8;
 static_assert(kT32 * kKStrF + kT32 * kVStrF + kWavesF * 4 * 64 * 4 <= 160 * 1024, "LDS budget");
-
-// K slot of tile key kap (0..31): key g + 16b + 4j sits in slot 16b + 4g + j.
-__device__ __forceinline__ int kslot32(int kap) {
-    const int b = kap >> 4, r = kap & 15;
-    return 16 * b + 4 * (r & 3) + (r >> 2);
-}
 
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_f32_kernel(AttnArgs a, int n_hg) {
@@ -137,7 +129,7 @@ attn_f32_kernel(AttnArgs a, int n_hg) {
     // Online-softmax state (per lane: head l16) and the wave's 64 output columns 64 w + 16 cb +
     // 4 g + 0..3 of head l16.
     float m = sink;
-    float ref = (sink == -INFINITY) ? 0.0f : sink;
+    float ref = f32_ref(sink);
     float l = expf(sink - ref);
     f32x4 acc[4] = {};
 
@@ -179,33 +171,22 @@ attn_f32_kernel(AttnArgs a, int n_hg) {
             dma_k(iv_next);   // K(t+1), during the softmax and the values
         }
         // ---- scores: the four quarters in order; lane (g, l16): keys g + 4e of the tile
-        float s[8];
-        float mt = -INFINITY;
+        float tot[8];
 #pragma unroll
         for (int bb = 0; bb < 2; bb++) {
             const f32x4 p0 = part_lds[0][bb][lane], p1 = part_lds[1][bb][lane];
             const f32x4 p2 = part_lds[2][bb][lane], p3 = part_lds[3][bb][lane];
 #pragma unroll
-            for (int j = 0; j < 4; j++) {
-                const int e = 4 * bb + j;
-                const float tot = ((p0[j] + p1[j]) + p2[j]) + p3[j];
-                s[e] = t * kT32 + g + 4 * e < n ? tot * scale : -INFINITY;
-                mt = fmaxf(mt, s[e]);
-            }
+            for (int j = 0; j < 4; j++) tot[4 * bb + j] = f32_score_sum(p0[j], p1[j], p2[j], p3[j]);
         }
-        mt = max_xor32(max_xor16(mt));
+        float s[8];
+        const float mt = f32_tile_scores(tot, t * kT32 + g, n, scale, s);
         const float m_new = fmaxf(m, mt);
-        const float ref_new = (m_new == -INFINITY) ? 0.0f : m_new;
+        const float ref_new = f32_ref(m_new);
         const float alpha = expf(m - ref_new);
         float pe[8];
-        float psum = 0.0f;
-#pragma unroll
-        for (int e = 0; e < 8; e++) {
-            pe[e] = s[e] == -INFINITY ? 0.0f : expf(s[e] - ref_new);
-            psum += pe[e];
-        }
-        psum = sum_xor32(sum_xor16(psum));
-        l = alpha * l + psum;
+        const float psum = f32_tile_weights(s, ref_new, pe);
+        l = f32_l_step(alpha, l, psum);
         m = m_new;
         ref = ref_new;
 #pragma unroll
@@ -247,6 +228,7 @@ attn_f32_kernel(AttnArgs a, int n_hg) {
 }  // namespace
 
 hipError_t launch_attn_f32(const AttnArgs &a, hipStream_t s) {
+    if (f32_split_applies(a.rows, a.H, a.kmax)) return launch_attn_f32_split(a, s);
     const int n_hg = (a.H + 15) / 16;
     const int64_t grid = (int64_t)a.rows * n_hg;
     if (grid == 0) return hipSuccess;

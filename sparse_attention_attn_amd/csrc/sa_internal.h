@@ -73,11 +73,30 @@ AttnPlan plan_attn_bf16(int64_t rows, int H, int32_t kmax);
 size_t split_workspace_bytes(int64_t rows, int H, int32_t kmax);
 hipError_t launch_attn_split(const AttnArgs &a, hipStream_t s);
 
+// The float32 split path (sa_attn_f32_split.hip) for small batches: launches with fewer than
+// kF32SplitMaxUnits (row, 64-head block) pairs and index lists of more than kF32SplitMinK (and
+// at most kSplitMaxK) entries, a subset of the bf16 split's launches, so that
+// sparse_attn_workspace_bytes, which has no dtype, stays an upper bound. Measured on 64 heads at
+// k = 640: 24 us at 1 row, 35 at 8 and 66 at 16 against about 83 us for attn_f32_kernel; at 23
+// rows its values kernel would run three waves of workgroups. Index lists of at most four tiles
+// are as fast in attn_f32_kernel. The score tiles take rows x ceil(kmax / 32) x ceil(H / 16) x
+// 2 KiB of workspace, never more than the bf16 split's. Both float32 paths give the same bits.
+constexpr int64_t kF32SplitMaxUnits = 17;
+constexpr int32_t kF32SplitMinK = 128;
+static_assert(kF32SplitMaxUnits <= kSplitMaxUnits, "the float32 split's launches are the bf16 split's");
+bool f32_split_applies(int64_t rows, int H, int32_t kmax);
+size_t f32_split_workspace_bytes(int64_t rows, int H, int32_t kmax);
+hipError_t launch_attn_f32_split(const AttnArgs &a, hipStream_t s);
+
 // Compute units of the current device, cached per device (256 if the query fails).
 int device_cu_count();
 
 // The validated decode call behind sparse_attn_decode (for the allocation-free variant in
-// sa_noalloc.hip), and a way for that file to set the calling thread's last error.
+// sa_noalloc.hip), its validation alone (nothing enqueued, no HIP call), and a way for that file
+// to set the calling thread's last error.
+int check_decode(int dtype, const void *q, const void *k_cache, const void *v_cache, int64_t n_ctx, const int32_t *idx,
+                 const int32_t *nsel, int32_t kmax, const float *sinks, float scale, int32_t B, int32_t H, int32_t D,
+                 float *out, void *ws, size_t ws_bytes);
 int run_decode(int dtype, const void *q, const void *k_cache, const void *v_cache, int64_t n_ctx, const int32_t *idx,
                const int32_t *nsel, int32_t kmax, const float *sinks, float scale, int32_t B, int32_t H, int32_t D,
                float *out, void *ws, size_t ws_bytes, void *stream);

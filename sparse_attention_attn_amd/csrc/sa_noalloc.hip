@@ -7,8 +7,8 @@
 // device current, by hipGetSymbolAddress; only that address is ever passed to a kernel (the
 // array's name is a host-side stand-in on the host). Every call on one GPU shares the array, so
 // two calls in flight at once on one GPU (on different streams, or from different threads) race.
-// The kernels that use it (the split path's score tiles) write every byte they read in the same
-// call, so nothing has to be cleared between calls.
+// The kernels that use it (the bf16 and float32 split paths' score tiles) write every byte they
+// read in the same call, so nothing has to be cleared between calls.
 #include <hip/hip_runtime.h>
 
 #include <cstdio>
@@ -44,13 +44,26 @@ extern "C" int sparse_attn_decode_noalloc(int dtype, const void *q, const void *
                                           int64_t n_ctx, const int32_t *idx, const int32_t *nsel, int32_t kmax,
                                           const float *sinks, float scale, int32_t B, int32_t H, int32_t D,
                                           float *out, void *stream) {
-    const size_t need = dtype == SA_BF16 ? sparse_attn_workspace_bytes(SA_OP_DECODE, B, H, D, kmax, n_ctx) : 0;
+    // The workspace this call needs (run_decode validates every argument; sizes it would refuse
+    // need none here).
+    size_t need = 0;
+    if (dtype == SA_BF16)
+        need = sparse_attn_workspace_bytes(SA_OP_DECODE, B, H, D, kmax, n_ctx);
+    else if (dtype == SA_F32 && B > 0 && H >= 1 && H <= SA_MAX_HEADS && kmax >= 1 && kmax <= SA_MAX_KMAX &&
+             sa::f32_split_applies(B, H, kmax))
+        need = sa::f32_split_workspace_bytes(B, H, kmax);
     if (need > kScratchBytes) {
         char msg[160];
         snprintf(msg, sizeof msg, "this call needs %zu bytes of workspace, more than the %zu of the static scratch",
                  need, kScratchBytes);
         return sa::fail_with(SA_ERR_WORKSPACE, msg);
     }
+    // Every argument is checked before the scratch's address is looked up (a HIP call), so that
+    // an invalid call reports its own status; the placeholder only stands for that address.
+    void *const placeholder = reinterpret_cast<void *>(uintptr_t{256});
+    const int rc = sa::check_decode(dtype, q, k_cache, v_cache, n_ctx, idx, nsel, kmax, sinks, scale, B, H, D, out,
+                                    need > 0 ? placeholder : nullptr, need > 0 ? kScratchBytes : 0);
+    if (rc != SA_OK) return rc;
     void *ws = nullptr;
     if (need > 0) {
         int dev = -1;

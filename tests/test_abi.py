@@ -242,6 +242,15 @@ def test_noalloc_validation():
     assert lib.sparse_attn_decode_noalloc(*bad) == L.SA_ERR_NULL
     bad = list(args); bad[7] = 0
     assert lib.sparse_attn_decode_noalloc(*bad) == L.SA_ERR_SHAPE
+    # Float32 at split-path sizes: the workspace is worked out only for valid sizes, so invalid
+    # ones get their own status (nothing is launched for any of these).
+    f32 = [L.SA_F32, A16, A16, A16, 4096, A16, None, 640, A16, 0.04, 8, 64, 512, A16, None]
+    for i, val, code in [(10, -1, L.SA_ERR_SHAPE), (11, 0, L.SA_ERR_SHAPE), (7, 0, L.SA_ERR_SHAPE),
+                         (1, None, L.SA_ERR_NULL), (12, 256, L.SA_ERR_UNSUPPORTED)]:
+        bad = list(f32); bad[i] = val
+        assert lib.sparse_attn_decode_noalloc(*bad) == code, (i, val)
+    zero = list(f32); zero[10] = 0
+    assert lib.sparse_attn_decode_noalloc(*zero) == L.SA_OK
 
 
 def test_gather_probe_validation():

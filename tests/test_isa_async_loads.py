@@ -3,8 +3,8 @@ destination registers fill in asynchronously: the compiler sees a finished value
 load, so nothing stops it from copying or spilling those registers before the data has
 arrived. The kernels are correct only if it never does, i.e. if every instruction that
 touches such a destination comes after an `s_waitcnt vmcnt` (the explicit waits that cover
-the loads). This compiles csrc/sa_attn.hip, csrc/sa_attn_split.hip and csrc/sa_attn_f32.hip to gfx950 assembly
-with the library's own flags and checks that, for every kernel, along the code that follows
+the loads). This compiles csrc/sa_attn.hip, csrc/sa_attn_split.hip, csrc/sa_attn_f32.hip and
+csrc/sa_attn_f32_split.hip to gfx950 assembly with the library's own flags and checks that, for every kernel, along the code that follows
 each such load.
 """
 import os
@@ -86,7 +86,7 @@ def test_parser_finds_an_early_copy():
 
 
 @pytest.mark.parametrize("src,tag", [("sa_attn.hip", "attn_bf16"), ("sa_attn_split.hip", "attn_split"),
-                                     ("sa_attn_f32.hip", "attn_f32")])
+                                     ("sa_attn_f32.hip", "attn_f32"), ("sa_attn_f32_split.hip", "attn_f32_split")])
 def test_async_query_loads_are_not_touched_before_a_wait(tmp_path, src, tag):
     out = tmp_path / (src + ".s")
     cmd = [HIPCC, *B.HIP_FLAGS, *B.COMMON, "--cuda-device-only", "-S",

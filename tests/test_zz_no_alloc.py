@@ -1,8 +1,8 @@
 """sparse_attn_decode_noalloc (the decode call whose workspace is the library's static scratch, for
 callers that cannot allocate) against sparse_attn_decode with a caller-allocated workspace, through
 the C ABI: bit for bit on two calls in a row, the second with a smaller input, so the second call
-runs on scratch that still holds the first call's contents. A large batch (no workspace) and a
-float32 call (none either) go through it too."""
+runs on scratch that still holds the first call's contents, for the bf16 and the float32 split
+paths. A large batch and a float32 call with a short index list (no workspace) go through it too."""
 import ctypes
 import sys
 
@@ -29,8 +29,6 @@ def _call_both(case):
     d = to_device(case, DEV)
     code = L.SA_BF16 if case.dtype == "bf16" else L.SA_F32
     need = lib.sparse_attn_workspace_bytes(L.SA_OP_DECODE, case.rows, case.heads, 512, case.kmax, case.n_ctx)
-    if code == L.SA_F32:
-        need = 0
     ws = torch.empty(max(need, 1), dtype=torch.uint8, device=DEV)
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     ref = torch.full((case.rows, case.heads, 512), 7.0, device=DEV)
@@ -65,9 +63,25 @@ def test_noalloc_equals_decode_twice(first, second):
         say(f"  ok (bit-equal to sparse_attn_decode) {st}")
 
 
+def test_noalloc_f32_split_twice():
+    """The float32 split path (score tiles through the scratch), then a smaller float32 split launch."""
+    for i, kw in enumerate((dict(seed=505, batch=8, heads=64, n_ctx=4096, k=640),
+                            dict(seed=506, batch=2, heads=32, n_ctx=1000, k=300))):
+        case = w.decode_f32(**kw)
+        if i == 1:
+            case.nsel[0] = kw["k"] // 2
+            case.idx[0, kw["k"] // 2:] = -1
+        say(f"f32 call {i + 1}: B={case.rows} H={case.heads} N={case.n_ctx} k={case.kmax}")
+        need, ref, got = _call_both(case)
+        assert np.array_equal(ref.view(np.int32), got.view(np.int32)), f"f32 call {i + 1}: noalloc differs"
+        rows = [0, case.rows - 1]
+        st = assert_parity(got[rows], run_oracle(case, rows=rows)[rows], *F32_TOL, f"noalloc f32 call {i + 1}")
+        say(f"  ok (bit-equal to sparse_attn_decode) {st}")
+
+
 def test_noalloc_without_workspace_paths():
-    """Calls that need no workspace (a large batch on the persistent kernels, and float32) go through
-    unchanged."""
+    """Calls that need no workspace (a large batch on the persistent kernels, and float32 with a
+    short index list) go through unchanged."""
     case = w.decode_bf16(seed=504, batch=64, heads=64, n_ctx=700, k=200)
     need, ref, got = _call_both(case)
     assert need == 0 and np.array_equal(ref.view(np.int32), got.view(np.int32))
