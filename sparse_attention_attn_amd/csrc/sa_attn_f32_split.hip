@@ -22,12 +22,13 @@
 //      layout (lane (g, l16): tile keys g + 4e of head l16), to the workspace:
 //      [row][tile][16-head group][lane][8] fp32, 2 KiB per tile and head group.
 //   2. attn_f32_split_values_kernel: one workgroup per (row, 16-head group, 64-column slice),
-//      four waves, one 16-column block each. In rounds of up to twelve tiles, the round's score
-//      tiles and V column slices come into LDS together; then (a) each wave scales and masks
-//      the scores of every fourth tile and takes their maxima, (b) every wave walks the running
-//      maximum over the round's tiles (each tile's reference and alpha), and each wave weighs
-//      its own tiles, and (c) every wave runs the tile sums, rescales and value MFMAs in key
-//      order, as attn_f32_kernel does for its columns.
+//      four waves, one 16-column block each, in rounds of up to twelve tiles. Each wave gathers
+//      its own columns of the round's V rows and loads the score sums of its share of the tiles;
+//      then (a) each wave scales and masks the scores of every fourth tile and takes their
+//      maxima, (b) every wave walks the running maximum over the round's tiles (each tile's
+//      reference and alpha), and each wave weighs its own tiles, and (c) every wave runs the
+//      tile sums, rescales and value MFMAs in key order, as attn_f32_kernel does for its
+//      columns, refilling its V slots with the next round's tiles as it goes.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -41,13 +42,11 @@ namespace {
 
 constexpr int kSplitColsF = 64;                  // output columns per values workgroup
 constexpr int kSlicesF = kHeadDim / kSplitColsF;
-constexpr int kVSliceF = kSplitColsF * 4;        // bytes of a key's V row slice
-constexpr int kVTileF = kT32 * kVSliceF;         // one tile's V slices: 8 KiB
 constexpr int kSTileF = 64 * 8 * 4;              // one tile's scores for a 16-head group: 2 KiB
 constexpr int kRingF = 12;                       // tiles per round of the values kernel
 constexpr int kMineF = kRingF / 4;               // tiles each of the four waves scales and weighs
 static_assert(kRingF % 4 == 0, "every wave weighs the same number of a round's tiles");
-static_assert(kRingF * (kVTileF + kSTileF + 2 * 64 * 4) + kSplitMaxK * 4 <= 150 * 1024, "LDS budget");
+static_assert(kRingF * (kT32 * kSplitColsF * 4 + kSTileF + 2 * 64 * 4) + kSplitMaxK * 4 <= 150 * 1024, "LDS budget");
 
 // LDS pointer from a 32-bit LDS byte address.
 template <typename T>
@@ -173,23 +172,21 @@ attn_f32_split_scores_kernel(AttnArgs a, int ntiles_max, int n_hb, int n_hg) {
     }
 }
 
-// LDS byte offset, within a tile's V slices, of column c (0..63 of the slice) of tile key r.
-// Key r's 256-byte slice holds its 16-byte chunk q at chunk q ^ 4(r & 3), so that the four keys
-// one value read takes (lane groups g = 0..3: keys 4st + g) sit on four different bank ranges.
-__device__ __forceinline__ uint32_t vslice_at(int r, int c) {
-    return (uint32_t)(r * kVSliceF + (((c >> 2) ^ (4 * (r & 3))) << 4) + ((c & 3) << 2));
-}
-
 // One workgroup per (row, 16-head group, 64-column slice), in an order that keeps the
 // workgroups of one row and head group on one XCD (they read the same score tiles). Four waves:
-// wave w owns the 16 columns cs*64 + 16w .. +15 (one MFMA block).
+// wave w owns the 16 columns cs*64 + 16w .. +15 (one MFMA block) and gathers only those columns
+// of every selected V row, into LDS slots of its own (32 keys x 64 bytes per tile: the four keys
+// one value read takes sit in one 256-byte window, on distinct banks). A wave's slot of a tile
+// is then free as soon as its own value MFMAs of that tile have read it: the next round's V
+// slices go out in the value phase, tile by tile, with no barrier, and the wave's share of the
+// next round's score tiles is loaded into registers in the same phase.
 __global__ void __launch_bounds__(256)
 attn_f32_split_values_kernel(AttnArgs a, int ntiles_max, int n_hg) {
-    __shared__ __attribute__((aligned(16))) char v_lds[kRingF * kVTileF];
-    // A tile's raw score sums, then (same slot, same lane layout: 32 bytes per lane) its weights.
-    __shared__ __attribute__((aligned(16))) char s_lds[kRingF * kSTileF];
-    __shared__ float mt_lds[kRingF][64];    // per tile: its maximum
-    __shared__ float psum_lds[kRingF][64];  // per tile: its sum
+    constexpr int kVPriv = kT32 * 16 * 4;   // a wave's 16 columns of a tile: 2 KiB
+    __shared__ __attribute__((aligned(16))) char v_lds[kRingF][4][kVPriv];
+    __shared__ f32x4 pe_lds[kRingF][64][2];  // per tile: its weights, lane layout (keys g + 4e)
+    __shared__ float mt_lds[kRingF][64];     // per tile: its maximum
+    __shared__ float psum_lds[kRingF][64];   // per tile: its sum
     __shared__ int idx_lds[kSplitMaxK];
     __shared__ int bad_lds[4];
 
@@ -204,23 +201,29 @@ attn_f32_split_values_kernel(AttnArgs a, int ntiles_max, int n_hg) {
     const int head = 16 * hg + l16;
     const bool head_ok = head < a.H;
 
-    // First memory round trip: the first round's score tiles, the row's index list (the first
-    // ntiles_max * 32 entries, the offsets clamped to the row), the sink and the row's count,
-    // all in flight together. Score tiles past the row's count are never written by the scores
-    // kernel; reading them stays inside the workspace, and they are not used.
-    const int nt_first = ntiles_max < kRingF ? ntiles_max : kRingF;
+    // This wave's raw score sums of the tiles w, w + 4, w + 8 of the round starting at tile t0
+    // (lane layout: 32 bytes per lane); tiles past ntiles_max are not read. Tiles past the row's
+    // count are never written by the scores kernel; reading them stays inside the workspace, and
+    // they are not used.
     const float *sws = (const float *)a.ws + score_block_f32(row, 0, hg, ntiles_max, n_hg);
-    const uint32_t v_base = lds_addr((SA_LDS char *)v_lds);
-    const uint32_t s_base = lds_addr((SA_LDS char *)s_lds);
-    // Each wave moves 512 bytes of every 2 KiB score tile, in two 256-byte pieces.
-    auto issue_scores = [&](int t, int slot) {
-        const uint32_t off = (uint32_t)t * (uint32_t)(n_hg * kSTileF) + 512u * w + 4u * lane;
-        dma4(sws, off, s_base + slot * kSTileF + 512 * w);
-        dma4(sws, off + 256u, s_base + slot * kSTileF + 512 * w + 256);
+    f32x4 sraw[kMineF][2];
+    auto load_scores = [&](int t0) {
+#pragma unroll
+        for (int j = 0; j < kMineF; j++) {
+            const int t = t0 + w + 4 * j;
+            if (t < ntiles_max) {
+                const f32x4 *src = (const f32x4 *)(sws + (size_t)t * n_hg * (kSTileF / 4) + lane * 8);
+                sraw[j][0] = src[0];
+                sraw[j][1] = src[1];
+            }
+        }
     };
-    for (int i = 0; i < nt_first; i++) issue_scores(i, i);
-    // Index list: piece j (64 entries) goes to wave j & 3; pieces past the list are not issued.
-    const int npieces = (ntiles_max * kT32 + 63) / 64;
+
+    // First memory round trip: this wave's score sums of the first round, the row's index list
+    // (the first ntiles_max * 32 entries, the offsets clamped to the row), the sink and the
+    // row's count, all in flight together.
+    load_scores(0);
+    const int npieces = (ntiles_max * kT32 + 63) / 64;  // index pieces of 64 entries; piece j: wave j & 3
     for (int j = w; j < npieces; j += 4) {
         const int pp = j * 64 + lane;
         const int pc = pp < a.kmax ? pp : a.kmax - 1;
@@ -240,58 +243,39 @@ attn_f32_split_values_kernel(AttnArgs a, int ntiles_max, int n_hg) {
     f32x4 acc = {};
     const float scale = a.scale;
 
+    const int64_t col_b = ((int64_t)cs * kSplitColsF + 16 * w) * 4;  // byte offset of the wave's columns
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)((const char *)a.v + row * a.cache_stride * 4 + (int64_t)cs * kVSliceF), 0,
-        (int)(uint32_t)(a.n_ctx * kRowF - (int64_t)cs * kVSliceF), kBufferFlags);
-    // DMA lane roles: one DMA moves four keys' slices (1 KiB); lane l moves the source chunk
-    // (l & 15) ^ 4(l >> 4) of key 4q + (l >> 4) into chunk l & 15 of that key's slice. Wave w
-    // moves the key quads q = w and w + 4 of every tile.
-    const uint32_t src_chunk = (uint32_t)(((lane & 15) ^ (4 * (lane >> 4))) << 4);
+        (void *)((const char *)a.v + row * a.cache_stride * 4 + col_b), 0, (int)(uint32_t)(a.n_ctx * kRowF - col_b),
+        kBufferFlags);
+    const uint32_t v_base = lds_addr((SA_LDS char *)&v_lds[0][w][0]);
     // An entry inside the count that is out of range makes the whole row NaN, as in
-    // attn_f32_kernel (bad_w: one of this wave's entries is); masked entries gather zeros.
+    // attn_f32_kernel (bad_w: one of the row's entries is; every wave sees every entry).
     bool bad_w = false;
+    // Tile t's V columns of this wave into slot i: two DMAs of sixteen keys; lane l moves the
+    // 16-byte chunk l & 3 of key 16h + (l >> 2) (masked or out-of-range entries gather zeros).
+    auto issue_v = [&](int t, int i) {
+#pragma unroll
+        for (int h = 0; h < 2; h++) {
+            const int pos = t * kT32 + 16 * h + (lane >> 2);
+            const int raw = pos < n ? idx_lds[pos] : -1;
+            const bool inr = raw >= 0 && (int64_t)raw < a.n_ctx;
+            bad_w = bad_w || __builtin_amdgcn_ballot_w64(pos < n && !inr) != 0;
+            const int iv = inr ? raw : -1;  // -1: an offset past the range, zeros
+            dma16_buf(rv, ((uint32_t)iv << 11) + ((uint32_t)(lane & 3) << 4),
+                      v_base + (uint32_t)(i * 4 * kVPriv + h * 1024));
+        }
+    };
+    {
+        const int nt0 = ntiles < kRingF ? ntiles : kRingF;
+        for (int i = 0; i < nt0; i++) issue_v(i, i);
+    }
 
     for (int t0 = 0; t0 < ntiles; t0 += kRingF) {
         const int nt = ntiles - t0 < kRingF ? ntiles - t0 : kRingF;
-        // Second memory round trip: the round's V slices (and, after the first round, its score
-        // tiles). The index entries are read from LDS first, so the gathers go out back to back.
-        if (t0 > 0)
-            for (int i = 0; i < nt; i++) issue_scores(t0 + i, i);
-        int raw[kRingF][2];
-#pragma unroll
-        for (int i = 0; i < kRingF; i++) {
-#pragma unroll
-            for (int h = 0; h < 2; h++) {
-                const int pos = (t0 + i) * kT32 + 4 * (w + 4 * h) + (lane >> 4);
-                raw[i][h] = (i < nt && pos < n) ? idx_lds[pos] : -1;
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < kRingF; i++) {
-            if (i < nt) {
-#pragma unroll
-                for (int h = 0; h < 2; h++) {
-                    const int q = w + 4 * h;
-                    const int pos = (t0 + i) * kT32 + 4 * q + (lane >> 4);
-                    const bool inr = raw[i][h] >= 0 && (int64_t)raw[i][h] < a.n_ctx;
-                    bad_w = bad_w || __builtin_amdgcn_ballot_w64(pos < n && !inr) != 0;
-                    const int iv = inr ? raw[i][h] : -1;  // -1: an offset past the range, zeros
-                    dma16_buf(rv, ((uint32_t)iv << 11) + src_chunk, v_base + i * kVTileF + 4 * q * kVSliceF);
-                }
-            }
-        }
-        wait_vmcnt<0>();
-        lds_barrier();  // every wave's slices and score pieces have landed
+        wait_vmcnt<0>();  // this wave's V slices of the round (and its score loads) have landed
 
         // (a) Scaled scores and the maxima of this wave's tiles of the round (w, w + 4, w + 8).
         float sk[kMineF][8];
-        f32x4 sraw[kMineF][2];
-#pragma unroll
-        for (int j = 0; j < kMineF; j++) {
-            const SA_LDS f32x4 *sp = lds_ptr<f32x4>(s_base + (w + 4 * j) * kSTileF + lane * 32);
-            sraw[j][0] = sp[0];
-            sraw[j][1] = sp[1];
-        }
 #pragma unroll
         for (int j = 0; j < kMineF; j++) {
             const int i = w + 4 * j;
@@ -303,7 +287,7 @@ attn_f32_split_values_kernel(AttnArgs a, int ntiles_max, int n_hg) {
         }
         lds_barrier();
         // (b) The running maximum over the round's tiles in key order (every wave computes the
-        // same values), then the weights of this wave's tiles, written over their scores.
+        // same values), then the weights of this wave's tiles.
         float ref_t[kRingF], alpha_t[kRingF], mt_t[kRingF];
 #pragma unroll
         for (int i = 0; i < kRingF; i++) mt_t[i] = mt_lds[i][lane];
@@ -327,25 +311,27 @@ attn_f32_split_values_kernel(AttnArgs a, int ntiles_max, int n_hg) {
                     if (w == q) ref = ref_t[4 * j + q];
                 float pe[8];
                 const float psum = f32_tile_weights(sk[j], ref, pe);
-                SA_LDS f32x4 *pp = lds_ptr<f32x4>(s_base + i * kSTileF + lane * 32);
-                pp[0] = (f32x4){pe[0], pe[1], pe[2], pe[3]};
-                pp[1] = (f32x4){pe[4], pe[5], pe[6], pe[7]};
+                pe_lds[i][lane][0] = (f32x4){pe[0], pe[1], pe[2], pe[3]};
+                pe_lds[i][lane][1] = (f32x4){pe[4], pe[5], pe[6], pe[7]};
                 psum_lds[i][lane] = psum;
             }
         }
         lds_barrier();
+        // The next round's score sums go out now (sraw is free).
+        const int t1 = t0 + kRingF;
+        if (t1 < ntiles) load_scores(t1);
         // (c) Tile sums, rescales and value MFMAs in key order. The tile sums are read up front,
-        // and each tile's weights and value operands one tile ahead of its MFMAs.
+        // and each tile's weights and value operands one tile ahead of its MFMAs. Once tile i's
+        // MFMAs have read the wave's slot i, the next round's tile i goes into it.
         float psum_t[kRingF];
 #pragma unroll
         for (int i = 0; i < kRingF; i++) psum_t[i] = psum_lds[i][lane];
         auto operands = [&](int i, f32x4 &pa, f32x4 &pb, float (&vx)[8]) {
-            const SA_LDS f32x4 *pp = lds_ptr<f32x4>(s_base + i * kSTileF + lane * 32);
-            pa = pp[0];
-            pb = pp[1];
+            pa = pe_lds[i][lane][0];
+            pb = pe_lds[i][lane][1];
 #pragma unroll
             for (int st = 0; st < 8; st++)
-                vx[st] = *lds_ptr<float>(v_base + i * kVTileF + vslice_at(4 * st + g, 16 * w + l16));
+                vx[st] = *lds_ptr<float>(v_base + (uint32_t)(i * 4 * kVPriv + (4 * st + g) * 64 + l16 * 4));
         };
         f32x4 pa_c, pb_c;
         float vx_c[8];
@@ -363,14 +349,17 @@ attn_f32_split_values_kernel(AttnArgs a, int ntiles_max, int n_hg) {
                 const float pe[8] = {pa_c[0], pa_c[1], pa_c[2], pa_c[3], pb_c[0], pb_c[1], pb_c[2], pb_c[3]};
 #pragma unroll
                 for (int st = 0; st < 8; st++) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(vx_c[st], pe[st], acc, 0, 0, 0);
+                // Slot i has been read (its values are in vx_c, used above): refill it.
+                if (t1 + i < ntiles) issue_v(t1 + i, i);
                 pa_c = pa_n;
                 pb_c = pb_n;
 #pragma unroll
                 for (int st = 0; st < 8; st++) vx_c[st] = vx_n[st];
             }
         }
-        lds_barrier();  // every wave is done with this round's buffers
+        lds_barrier();  // every wave is done with this round's weights
     }
+    wait_vmcnt<0>();
 
     // Whole-row NaN for an out-of-range index (any wave saw one), else acc / l.
     if (lane == 0) bad_lds[w] = bad_w;
