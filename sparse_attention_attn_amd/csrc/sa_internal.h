@@ -77,7 +77,7 @@ hipError_t launch_attn_split(const AttnArgs &a, hipStream_t s);
 // kF32SplitMaxUnits (row, 64-head block) pairs and index lists of more than kF32SplitMinK (and
 // at most kSplitMaxK) entries, a subset of the bf16 split's launches, so that
 // sparse_attn_workspace_bytes, which has no dtype, stays an upper bound. Measured on 64 heads at
-// k = 640: 24 us at 1 row, 35 at 8 and 66 at 16 against about 83 us for attn_f32_kernel; at 23
+// k = 640: 23 us at 1 row, 35 at 8 and 64 at 16 against about 83 us for attn_f32_kernel; at 23
 // rows its values kernel would run three waves of workgroups. Index lists of at most four tiles
 // are as fast in attn_f32_kernel. The score tiles take rows x ceil(kmax / 32) x ceil(H / 16) x
 // 2 KiB of workspace, never more than the bf16 split's. Both float32 paths give the same bits.
