@@ -93,17 +93,21 @@ const char *sparse_attn_last_error(void);
  * Bytes of device workspace an attention call (op SA_OP_DECODE or SA_OP_PREFILL)
  * with these sizes needs; 0 for SA_OP_TOPK and for invalid sizes. Pass a buffer
  * of at least this size, 16-byte aligned, as ws / ws_bytes (NULL / 0 when it is
- * 0). The workspace is scratch for the call's kernels only: its contents before
- * and after a call mean nothing, and two calls in flight at once on different
- * streams need different workspaces.
+ * 0). The workspace is scratch for the call's kernels only: whatever it held
+ * before a call never changes the result, the caller needs neither to clear it
+ * nor to keep it, and two calls in flight at once (on different streams) need
+ * different workspaces.
  *
  * Small batches (fewer than 24 rows per block of 64 heads, index lists of at most
- * 1,024 entries) split the keys of every row across workgroups: each 64-key tile
- * is scored in its own workgroup and the raw scores go through the workspace
- * (rows x ceil(kmax / 64) x ceil(heads / 16) x 4 KiB), before the softmax and value
- * products fold them in key order. Larger batches need no workspace. A row's
- * result is the same, bit for bit, on either path (the ds4 commit log for
- * ds4_tp.c: a split that follows the launch must not change the output bytes).
+ * 1,024 entries) split the keys of every row across workgroups of one launch: each
+ * 64-key tile is scored in its own workgroup and the raw scores and tile maxima go
+ * through the workspace, before the softmax and value products fold them in key
+ * order. The workspace holds 6 KiB of sequence and ready words (the launch's
+ * workgroups wait on them; every call accepts any earlier contents), then
+ * rows x ceil(kmax / 64) x ceil(heads / 16) x 4,224 bytes. Larger batches need no
+ * workspace. A row's result is the same, bit for bit, on either path (the ds4
+ * commit log for ds4_tp.c: a split that follows the launch must not change the
+ * output bytes).
  * Float32 launches with fewer than 17 rows per block of 64 heads and index lists
  * of 129 to 1,024 entries split the same way, with 32-key tiles of 2 KiB (rows x
  * ceil(kmax / 32) x ceil(heads / 16) x 2 KiB, never more than the bf16 figure).

@@ -1,5 +1,5 @@
 // sa_attn_common.h -- the per-element arithmetic of the bf16 attention kernels, shared by the
-// persistent kernels (sa_attn.hip) and the split kernels for small batches (sa_attn_split.hip).
+// persistent kernels (sa_attn.hip) and the split path for small batches (sa_attn_split.hip).
 // Not part of the public ABI.
 //
 // What it computes: akol1/TensorFold pull request 4 ("DeepSeek V4.1: sparse attention on eight
@@ -75,7 +75,7 @@ __device__ __forceinline__ void half_start(HalfState &st, f32x4 (&acc)[CB], bool
 }
 
 // The pieces of one half tile's online-softmax step, in the order half_tile runs them. The
-// split kernels run the same pieces for a tile spread over waves and phases; every piece
+// split paths run the same pieces for a tile spread over workgroups, waves and phases; every piece
 // computes the same values from the same inputs, so the results are the same bits.
 //
 // Scaled scores (log2 units) of one half tile and their maximum over the wave's 32 keys. s0,

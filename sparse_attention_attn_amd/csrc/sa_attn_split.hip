@@ -1,6 +1,7 @@
 // sa_attn_split.hip -- the bf16 attention path for small batches: the keys of a row are split
 // across workgroups for the score contraction, and the softmax and value products then fold the
-// score tiles in key order. Same results, bit for bit, as the persistent kernels of sa_attn.hip.
+// score tiles in key order, all in one launch. Same results, bit for bit, as the persistent
+// kernels of sa_attn.hip.
 //
 // What it computes is the same as sa_attn.hip (akol1/TensorFold pull request 4, "DeepSeek V4.1:
 // sparse attention on eight SIMD groups, the same bytes", first commit message: 64-key tiles,
@@ -11,21 +12,42 @@
 //
 // Why: a row of the decode shape (64 heads, k = 640) is ten 64-key tiles. In the persistent
 // kernels one workgroup walks them in a chain, each tile waiting twice for rows gathered from
-// HBM, so a launch of one or a few rows takes about 30 us whatever the chip's size. Here:
-//   1. attn_split_scores_kernel: one workgroup per (row, tile, block of 64 heads). Its eight
-//      waves gather the tile's 64 K rows once and compute the score MFMA chain exactly as the
-//      persistent kernel does (same wave roles: key half kh = w >> 2, 16-head group w & 3; same
-//      K slot order and operand layout), then store each wave's raw scores, in its lane layout,
-//      to the workspace: [row][tile][16-head group][key half][lane][8] fp32, 4 KiB per tile and
-//      head group. All tiles of all rows run at once.
-//   2. attn_split_values_kernel: one workgroup per (row, 16-head group, 64-column slice). It
-//      loads the row's index list, gathers the V column slices of a round of up to ten tiles
-//      and their score tiles into LDS in one go, then runs, per wave (key half kh = w >> 2,
-//      16-column part w & 3), the same online-softmax steps and value MFMAs on each tile in
-//      order (the four waves of a key half share the weights), and the same fixed-order fold of
-//      the two key halves (sa_attn_common.h).
+// HBM, so a launch of one or a few rows takes about 30 us whatever the chip's size. Here every
+// workgroup of attn_split_kernel takes one or two roles:
+//   * producer of (row, tile, block of 64 heads): its eight waves gather the tile's 64 K rows
+//     once and run the score MFMA chain exactly as the persistent kernel does (same wave roles:
+//     key half kh = w >> 2, 16-head group w & 3; same K slot order and operand layout). The
+//     block's query goes through LDS once (64 KiB, one DMA per head). It stores each wave's raw
+//     scores, in its lane layout, and each key half's tile maximum per head, then publishes the
+//     tile's ready word.
+//   * consumer of (row, 16-head group, 64-column slice): it loads the row's index list and
+//     gathers the V column slices of a round of up to ten tiles while the producers run, waits
+//     for the ready words of the row's tiles, loads their scores and maxima, then runs, per wave
+//     (key half kh = w >> 2, 16-column part w & 3), the same online-softmax steps and value MFMAs
+//     on each tile in order (the four waves of a key half share the weights), and the same
+//     fixed-order fold of the two key halves (sa_attn_common.h).
 // Every (row, head, column) thus sees the same operations, on the same operands, in the same
 // order as in the persistent kernels: which path a launch takes never changes its bits.
+//
+// Workgroup order. All producers come first (padded to a multiple of eight), then the consumers,
+// remapped so that the consumers of one row and head group run on one XCD (the hardware places
+// workgroup i on XCD i % 8). A consumer therefore only ever waits for workgroups with lower ids,
+// which the hardware dispatches first (workgroups of a grid go out in id order) and which wait
+// for nothing. Every wait is also bounded in time: past 200 ms the row is reported as NaN.
+// (A layout that lets the first consumers of each row run the next row's producer tasks first,
+// so that eight decode rows need 266 workgroups instead of 336, measured slower: 15.9 against
+// 14.5 us; without the XCD remap, eight rows took 16.1 us.)
+//
+// Synchronisation through the workspace. Its first kSyncBytes hold, per (row, 64-head block),
+// a sequence number E, a consumer count U and one ready word per tile. Every workgroup reads E
+// at its start; a producer stores its scores and maxima with device-scope (sc1) stores, waits
+// until they have completed, and then stores the ready word ready_word(E, tile); a consumer
+// polls the ready words of its row's tiles with device-scope loads until all match, then reads
+// the scores with device-scope loads. The producer of tile 0 first resets U; the last consumer
+// of the group (the one that brings U to the group's consumer count) stores E + 1 after all its
+// reads, so the next launch on this workspace waits for different words. The words are mixed
+// with the tile index, so that no earlier contents of the workspace (zeros, a repeated byte,
+// data of another launch shape) can pass for a ready word except by a 64-bit coincidence.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -37,22 +59,39 @@
 namespace sa {
 namespace {
 
-constexpr int kSplitCols = 64;                 // output columns per values workgroup
+constexpr int kSplitCols = 64;                 // output columns per consumer
 constexpr int kSplitSlices = kHeadDim / kSplitCols;
 constexpr int kVRowB = kSplitCols * 2;         // bytes of a V row slice
 constexpr int kVTileB = kTile * kVRowB;        // one tile's V slices: 8 KiB
 constexpr int kSTileB = 2 * 64 * 8 * 4;        // one tile's scores for a 16-head group: 4 KiB
-constexpr int kRing = 10;                      // tiles per round of the values kernel
-static_assert(kSplitCols == 64 && kVRowB == 128, "the values kernel's waves own 16 columns each");
+constexpr int kMTileB = 2 * 16 * 4;            // one tile's maxima for a 16-head group: [key half][head]
+constexpr int kRing = 10;                      // tiles per round of a consumer
+constexpr int kMaxTiles = kSplitMaxK / kTile;
+static_assert(kSplitCols == 64 && kVRowB == 128, "a consumer's waves own 16 columns each");
+
+// Sync words: 32 per (row, 64-head block): [0] E, [1] U, [2 + t] the ready word of tile t.
+constexpr int kSyncGroupWords = 32;
+constexpr size_t kSyncBytes = (size_t)kSplitMaxUnits * kSyncGroupWords * 8;
+static_assert(2 + kMaxTiles <= kSyncGroupWords, "the ready words fit a group");
+// Bound of every wait: 200 ms of the 100 MHz constant clock (s_memrealtime).
+constexpr long long kWaitTicks = 20000000;
+
+__device__ __forceinline__ uint64_t ready_word(uint64_t e, int t) {
+    return (e + 1) ^ (0x9E3779B97F4A7C15ull * (uint64_t)(t + 1));
+}
 
 // Chunk swizzle of a V row slice in LDS (8 chunks of 16 bytes): the chunk c of the slice in
 // slot s is stored at chunk c ^ (s & 7). The four keys one 16-lane group reads in a
 // transposing read sit in four consecutive slots, which then use four different chunks.
 __device__ __forceinline__ int vswz(int s) { return s & 7; }
 
-// Score tiles: [row][tile][head group][key half][lane][8] fp32.
+// Workspace after the sync words: score tiles [row][tile][head group][key half][lane][8] fp32,
+// then tile maxima [row][tile][head group][key half][head] fp32.
 __device__ __forceinline__ size_t score_block(int64_t row, int tile, int hg, int ntiles_max, int n_hg) {
     return (((size_t)row * ntiles_max + tile) * n_hg + hg) * (kSTileB / 4);
+}
+__device__ __forceinline__ size_t maxima_offset(int64_t rows, int ntiles_max, int n_hg) {
+    return kSyncBytes + (size_t)rows * ntiles_max * n_hg * kSTileB;
 }
 
 // The row's count, by a scalar (constant address space) load: it waits on the scalar counter,
@@ -62,87 +101,164 @@ __device__ __forceinline__ int row_count(const AttnArgs &a, int64_t row) {
     return n < 0 ? 0 : (n > a.kmax ? a.kmax : n);
 }
 
-// One workgroup per (row, tile, block of 64 heads), blocks fastest. A tile past the row's
-// count has no selected key: its workgroup leaves at once (the values kernel never reads it).
-__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
-attn_split_scores_kernel(AttnArgs a, int ntiles_max, int n_hb, int n_hg) {
-    __shared__ __attribute__((aligned(16))) char k_lds[kTile * kKStride];
-    __shared__ int idx_lds[kWaves][64];
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+// Direct-to-LDS load of 4 bytes per lane at device scope (sc1: it reads what another
+// workgroup's device-scope stores left, never a stale cached copy), from sbase + voff_i to LDS
+// address lds + 4 i. sbase is taken from the first active lane.
+__device__ __forceinline__ void dma4_device(const void *sbase, uint32_t voff, uint32_t lds) {
+    const uint64_t p = (uint64_t)(uintptr_t)sbase;
+    const uint64_t pu = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)p) |
+                        ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(p >> 32)) << 32);
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2 sc1"
+                 ::"s"(lds), "v"(voff), "s"(pu) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+constexpr int kStoreDevice = 16;   // cache policy sc1 of a buffer store: device scope
 
+// LDS of the two roles, one array (a workgroup takes one role).
+// Consumer: V ring, score/weight ring, maxima, tile sums, index list, fold metadata, the fold
+// exchange, bad-index flags. Producer: K tile, index lists, the block's query.
+constexpr int kOffV = 0;
+constexpr int kOffS = kOffV + kRing * kVTileB;
+constexpr int kOffMax = kOffS + kRing * kSTileB;
+constexpr int kOffPsum = kOffMax + kRing * kMTileB;
+constexpr int kOffIdx = kOffPsum + 2 * kRing * 64 * 4;
+constexpr int kOffMeta = kOffIdx + kSplitMaxK * 4;
+constexpr int kOffXch = kOffMeta + 4 * 3 * 16 * 4;
+constexpr int kOffBad = kOffXch + 4 * 64 * 16;
+constexpr int kLdsConsumer = kOffBad + kWaves * 4;
+constexpr int kOffPIdx = kTile * kKStride;
+constexpr int kOffQ = kOffPIdx + kWaves * 64 * 4;
+constexpr int kLdsProducer = kOffQ + 64 * kRowBytes;
+constexpr int kLdsBytes = kLdsConsumer > kLdsProducer ? kLdsConsumer : kLdsProducer;
+static_assert(kLdsBytes <= 160 * 1024, "LDS of one workgroup");
+
+// Producer task b of the launch: (row, tile, head block), head blocks fastest.
+__device__ __forceinline__ void producer(const AttnArgs &a, char *lds, int64_t b, int ntiles_max, int n_hb, int n_hg,
+                                         uint64_t *sync) {
+    char *k_lds = lds;
+    int (*idx_lds)[64] = (int (*)[64])(lds + kOffPIdx);
+    char *q_lds = lds + kOffQ;
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int g = lane >> 4;
     const int l16 = lane & 15;
     const int wi = w & 3;
     const int kh = w >> 2;
-    const int64_t b = blockIdx.x;
     const int hb = (int)(b % n_hb);
     const int tile = (int)((b / n_hb) % ntiles_max);
     const int64_t row = b / ((int64_t)n_hb * ntiles_max);
     const int hg = 4 * hb + wi;
+    uint64_t *sg = sync + (row * n_hb + hb) * kSyncGroupWords;
 
-    // The query, the tile's index list and the row's count go out together (one memory round
-    // trip); a tile past the count then leaves, once its loads have landed.
-    bf16x8 qreg[16];
-    float sink_unused;
-    load_q_async(a, row, 16 * hg, g, l16, qreg, sink_unused);
+    // First memory round trip: E, the tile's index list and the row's count; the block's query
+    // follows (64 heads x 1 KiB into LDS, wave w moving heads 8w .. 8w+7) and may still be in
+    // flight while the K rows are gathered. Head h's row is stored rotated by h chunks of 16
+    // bytes, so that 16 heads read at one column hit 16 different bank groups.
+    const uint64_t e = __hip_atomic_load(sg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     {
         const int p = tile * kTile + lane;
         const int pc = p < a.kmax ? p : a.kmax - 1;
         dma4(a.idx + row * a.kmax, (uint32_t)pc * 4u, lds_addr(&idx_lds[w][0]));
     }
-    const int n = row_count(a, row);
-    wait_vmcnt<0>();
-    if (tile * kTile >= n) return;
-    q_ready(qreg, sink_unused);
-    __builtin_amdgcn_s_waitcnt(0);
-    // Row to gather for entry tile*64 + lane, or -1 (masked or out of range: gathers zeros,
-    // as in the persistent kernels; the values kernel marks a row with a live out-of-range
-    // entry as NaN).
-    const int iv_raw = idx_lds[w][lane];
-    const bool live = tile * kTile + lane < n;
-    const int iv = (live && iv_raw >= 0 && (int64_t)iv_raw < a.n_ctx) ? iv_raw : -1;
-
-    // Wave w gathers tile keys 8w .. 8w+7 (its key half) into the K slots of the persistent
-    // kernels: key 32kh + kap goes to slot 32kh + kslot_of_key(kap).
-    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)((const char *)a.k + row * a.cache_stride * 2), 0, (int)(uint32_t)(a.n_ctx * kRowBytes), kBufferFlags);
 #pragma unroll
-    for (int i = 0; i < kRows; i++) {
-        const int ij = __builtin_amdgcn_readlane(iv, kRows * w + i);
-        const int slot = 32 * kh + kslot_of_key(8 * wi + i);
-        dma16_buf(rk, ((uint32_t)ij << 10) + ((uint32_t)lane << 4), lds_addr((SA_LDS char *)k_lds + slot * kKStride));
+    for (int i = 0; i < 8; i++) {
+        const int hl = 8 * w + i;
+        const int h = 64 * hb + hl;
+        const void *src = h < a.H ? (const void *)((const uint16_t *)a.q + (row * a.H + h) * kHeadDim)
+                                  : (const void *)g_zero_row;
+        dma16(src, (uint32_t)((lane - hl) & 63) << 4, lds_addr(q_lds + hl * kRowBytes));
     }
+    const int n = row_count(a, row);
+    wait_vmcnt<8>();  // E and the index list; the query's eight rows may still be in flight
+    // Tiles past the row's count have no selected key and no consumer waits for them; tile 0
+    // always publishes (its producer resets the group's consumer count).
+    const int nwait = n > 0 ? (n + kTile - 1) / kTile : 1;
+    if (tile >= nwait) {
+        wait_vmcnt<0>();  // no DMA may land in LDS after this task
+        return;
+    }
+    if (tile * kTile < n) {
+        // Row to gather for entry tile*64 + lane, or -1 (masked or out of range: gathers zeros,
+        // as in the persistent kernels; the consumers mark a row with a live out-of-range entry
+        // as NaN).
+        const int iv_raw = idx_lds[w][lane];
+        const bool live = tile * kTile + lane < n;
+        const int iv = (live && iv_raw >= 0 && (int64_t)iv_raw < a.n_ctx) ? iv_raw : -1;
+        // Wave w gathers tile keys 8w .. 8w+7 (its key half) into the K slots of the persistent
+        // kernels: key 32kh + kap goes to slot 32kh + kslot_of_key(kap).
+        const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)((const char *)a.k + row * a.cache_stride * 2), 0, (int)(uint32_t)(a.n_ctx * kRowBytes),
+            kBufferFlags);
+#pragma unroll
+        for (int i = 0; i < kRows; i++) {
+            const int ij = __builtin_amdgcn_readlane(iv, kRows * w + i);
+            const int slot = 32 * kh + kslot_of_key(8 * wi + i);
+            dma16_buf(rk, ((uint32_t)ij << 10) + ((uint32_t)lane << 4),
+                      lds_addr((SA_LDS char *)k_lds + slot * kKStride));
+        }
+        wait_vmcnt<kRows>();  // this wave's query rows (its K rows may still be in flight)
+        lds_barrier();        // every wave's query rows have landed
+        bf16x8 qreg[16];      // lane (g, l16): head 16 wi + l16, dims 32 kk + 8 g + 0..7
+        {
+            const int hl = 16 * wi + l16;
+#pragma unroll
+            for (int kk = 0; kk < 16; kk++)
+                qreg[kk] = *lds_at<bf16x8>(lds_addr(q_lds + hl * kRowBytes) + (((4 * kk + g + hl) & 63) << 4));
+        }
+        wait_vmcnt<0>();
+        lds_barrier();  // every wave's K rows have landed
+        if (hg < n_hg) {
+            const SA_LDS char *krow = (const SA_LDS char *)k_lds + (32 * kh + l16) * kKStride + 16 * g;
+            f32x4 sacc0, sacc1;
+            score_chain(krow, qreg, sacc0, sacc1, [](int) {});
+            const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)((float *)((char *)a.ws + kSyncBytes) + score_block(row, tile, hg, ntiles_max, n_hg)), 0,
+                kSTileB, kBufferFlags);
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, sacc0), rs, (kh * 64 + lane) * 32, 0,
+                                                   kStoreDevice);
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, sacc1), rs, (kh * 64 + lane) * 32 + 16, 0,
+                                                   kStoreDevice);
+            // The half tile's maximum per head: tile_scores on the same operands as in the
+            // persistent kernels (the consumers take it instead of computing it).
+            float s_unused[8];
+            const float mt = tile_scores(sacc0, sacc1, tile * kTile + 32 * kh + 8 * g, n, (tile + 1) * kTile <= n,
+                                         a.scale * kLog2e, s_unused);
+            const __amdgpu_buffer_rsrc_t rm = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)((char *)a.ws + maxima_offset(a.rows, ntiles_max, n_hg) +
+                         (((size_t)row * ntiles_max + tile) * n_hg + hg) * kMTileB),
+                0, kMTileB, kBufferFlags);
+            if (g == 0)
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(mt), rm, (kh * 16 + l16) * 4, 0, kStoreDevice);
+        }
+    }
+    // Publish: every wave's device-scope stores have completed, then the tile's ready word (after
+    // the reset of the consumer count, for tile 0).
     wait_vmcnt<0>();
-    lds_barrier();  // every wave's K rows have landed
-    if (hg >= n_hg) return;
-
-    const SA_LDS char *krow = (const SA_LDS char *)k_lds + (32 * kh + l16) * kKStride + 16 * g;
-    f32x4 sacc0, sacc1;
-    score_chain(krow, qreg, sacc0, sacc1, [](int) {});
-    f32x4 *dst = (f32x4 *)((float *)a.ws + score_block(row, tile, hg, ntiles_max, n_hg) + (kh * 64 + lane) * 8);
-    dst[0] = sacc0;
-    dst[1] = sacc1;
+    lds_barrier();
+    if (w == 0 && lane == 0) {
+        if (tile == 0) __hip_atomic_store(sg + 1, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        wait_vmcnt<0>();
+        __hip_atomic_store(sg + 2 + tile, ready_word(e, tile), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
 }
 
-// One workgroup per (row, 16-head group, 64-column slice), in an order that keeps the
-// workgroups of one row and head group on one XCD (they read the same score tiles). Eight
+// Consumer task u of the launch: (row, 16-head group, 64-column slice), slices fastest. Eight
 // waves, two per SIMD: wave w takes key half kh = w >> 2 and the 16 columns cs*64 + 16(w & 3)
 // .. +15 (one MFMA block). The four waves of a key half split a round's tiles for the
-// expensive part of the online softmax (scaled scores, tile maxima, weights), share them
-// through LDS, and each runs the cheap sequential parts (reference scan, tile sums) itself.
-__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
-attn_split_values_kernel(AttnArgs a, int ntiles_max, int n_hg) {
-    __shared__ __attribute__((aligned(16))) char v_lds[kRing * kVTileB];
-    // A tile's scores, then (same slot, same lane layout: 32 bytes per lane and key half) its
-    // weights as the two bf16 parts of the value MFMA's P^T operand.
-    __shared__ __attribute__((aligned(16))) char s_lds[kRing * kSTileB];
-    __shared__ float mloc_lds[2][kRing][64];   // per key half and tile: the tile's maximum
-    __shared__ float psum_lds[2][kRing][64];   // per key half and tile: the tile sum
-    __shared__ int idx_lds[kSplitMaxK];
-    __shared__ float meta_lds[4][3][16];
-    __shared__ f32x4 xch_lds[4][64];
-    __shared__ int bad_lds[kWaves];
+// expensive part of the online softmax (scaled scores, weights), share the weights through
+// LDS, and each runs the cheap sequential parts (reference scan, tile sums) itself.
+__device__ __forceinline__ void consumer(const AttnArgs &a, char *lds, int64_t u, int ntiles_max, int n_hb, int n_hg,
+                                         uint64_t *sync) {
+    char *v_lds = lds + kOffV;
+    char *s_lds = lds + kOffS;
+    const float *max_lds = (const float *)(lds + kOffMax);   // [tile][key half][head]
+    float (*psum_lds)[kRing][64] = (float (*)[kRing][64])(lds + kOffPsum);
+    int *idx_lds = (int *)(lds + kOffIdx);
+    float (*meta_lds)[3][16] = (float (*)[3][16])(lds + kOffMeta);
+    f32x4 (*xch_lds)[64] = (f32x4 (*)[64])(lds + kOffXch);
+    int *bad_lds = (int *)(lds + kOffBad);
 
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -153,28 +269,16 @@ attn_split_values_kernel(AttnArgs a, int ntiles_max, int n_hg) {
     // Residue (mod 4) of the round's tiles this wave weighs: the two waves of a SIMD (w and
     // w ^ 4) take different residues, so every SIMD weighs five of ten tiles.
     const int qv = (cq + 2 * kh) & 3;
-    const int64_t u = xcd_remap(blockIdx.x, gridDim.x);
     const int cs = (int)(u % kSplitSlices);
     const int hg = (int)((u / kSplitSlices) % n_hg);
     const int64_t row = u / ((int64_t)kSplitSlices * n_hg);
     const int head = 16 * hg + l16;
+    const int hb = hg >> 2;
+    uint64_t *sg = sync + (row * n_hb + hb) * kSyncGroupWords;
 
-    // First memory round trip: the first round's score tiles, the row's index list (the first
-    // ntiles_max * 64 entries, the offsets clamped to the row), the sink and the row's count,
-    // all in flight together. Score tiles past the row's count are never written by the
-    // scores kernel; reading them stays inside the workspace, and they are not used.
-    const int nt_first = ntiles_max < kRing ? ntiles_max : kRing;
-    const float *sws = (const float *)a.ws + score_block(row, 0, hg, ntiles_max, n_hg);
-    const uint32_t v_base = lds_addr((SA_LDS char *)v_lds);
-    const uint32_t s_base = lds_addr((SA_LDS char *)s_lds);
-    // Each wave moves 512 bytes of every 4 KiB score tile, in two 256-byte pieces.
-    auto issue_scores = [&](int t, int slot) {
-        const uint32_t off = (uint32_t)t * (uint32_t)(n_hg * kSTileB) + 512u * w + 4u * lane;
-        dma4(sws, off, s_base + slot * kSTileB + 512 * w);
-        dma4(sws, off + 256u, s_base + slot * kSTileB + 512 * w + 256);
-    };
-    for (int i = 0; i < nt_first; i++) issue_scores(i, i);
-    // Index list: wave w moves tiles w and w + 8 (64 entries each) into LDS.
+    // First memory round trip: E, the row's index list (the first ntiles_max * 64 entries, the
+    // offsets clamped to the row), the sink and the row's count.
+    const uint64_t e = __hip_atomic_load(sg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
     for (int r = 0; r < 2; r++) {
         const int p = (w + 8 * r) * kTile + lane;
@@ -185,6 +289,7 @@ attn_split_values_kernel(AttnArgs a, int ntiles_max, int n_hg) {
     load4_async(sink, head < a.H ? a.sinks + head : (const float *)g_zero_row);
     const int n = row_count(a, row);
     const int ntiles = (n + kTile - 1) / kTile;
+    const int nwait = ntiles > 0 ? ntiles : 1;
     wait_vmcnt<0>();
     register_ready(sink);
     __builtin_amdgcn_s_waitcnt(0);
@@ -195,6 +300,11 @@ attn_split_values_kernel(AttnArgs a, int ntiles_max, int n_hg) {
     half_start(st, acc, kh == 0, sink);
     const float scale2 = a.scale * kLog2e;
 
+    const float *sws = (const float *)((const char *)a.ws + kSyncBytes) + score_block(row, 0, hg, ntiles_max, n_hg);
+    const float *mws = (const float *)((const char *)a.ws + maxima_offset(a.rows, ntiles_max, n_hg)) +
+                       ((size_t)row * ntiles_max * n_hg + hg) * (kMTileB / 4);
+    const uint32_t v_base = lds_addr((SA_LDS char *)v_lds);
+    const uint32_t s_base = lds_addr((SA_LDS char *)s_lds);
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
         (void *)((const char *)a.v + row * a.cache_stride * 2 + (int64_t)cs * kVRowB), 0,
         (int)(uint32_t)(a.n_ctx * kRowBytes - (int64_t)cs * kVRowB), kBufferFlags);
@@ -213,17 +323,12 @@ attn_split_values_kernel(AttnArgs a, int ntiles_max, int n_hg) {
         vaddr[t2] = (uint32_t)(slot * kVRowB + 16 * (chunk ^ vswz(slot)) + 8 * (l16 & 1));
     }
     // An entry inside the count that is out of range makes the whole row NaN, as in the
-    // persistent kernels (bad_w: one of this wave's entries is); masked entries (past the
-    // count) gather zeros.
+    // persistent kernels (bad_w: one of this wave's entries is, or its wait ran out); masked
+    // entries (past the count) gather zeros.
     bool bad_w = false;
-
-    for (int t0 = 0; t0 < ntiles; t0 += kRing) {
-        const int nt = ntiles - t0 < kRing ? ntiles - t0 : kRing;
-        // Second memory round trip: the round's V slices (and, after the first round, its
-        // score tiles). The round's index entries are read from LDS first, so that the gathers
-        // then go out back to back.
-        if (t0 > 0)
-            for (int i = 0; i < nt; i++) issue_scores(t0 + i, i);
+    // The V slices of a round: the round's index entries are read from LDS first, so that the
+    // gathers then go out back to back.
+    auto issue_v = [&](int t0, int nt) {
         int raw[kRing];
 #pragma unroll
         for (int i = 0; i < kRing; i++) {
@@ -240,15 +345,56 @@ attn_split_values_kernel(AttnArgs a, int ntiles_max, int n_hg) {
                 dma16_buf(rv, ((uint32_t)iv << 10) + dchunk, v_base + i * kVTileB + w * 1024);
             }
         }
-        wait_vmcnt<0>();
-        lds_barrier();  // every wave's slices and score pieces have landed
+    };
+    if (ntiles > 0) issue_v(0, ntiles < kRing ? ntiles : kRing);
 
-        // Phase 1: scaled scores and the tile maximum of this wave's tiles of the round (qv,
-        // qv + 4, qv + 8); the maxima go to LDS for the reference scan. Every LDS read of a phase
-        // goes out before the first use (a slot past the round's tiles is read and not used), so
-        // the reads' latencies overlap instead of adding up tile by tile.
+    // Wait until every tile of the row has been scored: wave 0 polls the ready words (lane t
+    // tile t), the others wait at the barrier. Bounded: past kWaitTicks the row is NaN.
+    if (w == 0) {
+        const long long t_start = wall_clock64();
+        bool late = false;
+        for (;;) {
+            bool pend = false;
+            if (lane < nwait) {
+                const uint64_t f = __hip_atomic_load(sg + 2 + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                pend = f != ready_word(e, lane);
+            }
+            if (__builtin_amdgcn_ballot_w64(pend) == 0) break;
+            if (wall_clock64() - t_start > kWaitTicks) {
+                late = true;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(2);
+        }
+        bad_w = bad_w || late;
+    }
+    lds_barrier();
+
+    for (int t0 = 0; t0 < ntiles; t0 += kRing) {
+        const int nt = ntiles - t0 < kRing ? ntiles - t0 : kRing;
+        if (t0 > 0) issue_v(t0, nt);
+        // The round's score tiles (each wave moves 512 bytes of every 4 KiB tile, in two
+        // 256-byte pieces) and maxima (wave w moves tiles w and w + 8), at device scope.
+        for (int i = 0; i < nt; i++) {
+            const uint32_t off = (uint32_t)(t0 + i) * (uint32_t)(n_hg * kSTileB) + 512u * w + 4u * lane;
+            dma4_device(sws, off, s_base + i * kSTileB + 512 * w);
+            dma4_device(sws, off + 256u, s_base + i * kSTileB + 512 * w + 256);
+        }
+#pragma unroll
+        for (int r = 0; r < 2; r++) {
+            const int i = w + 8 * r;
+            if (i < nt && lane < 32)
+                dma4_device(mws, (uint32_t)((t0 + i) * n_hg * kMTileB + 4 * lane),
+                            lds_addr((const char *)max_lds + i * kMTileB));
+        }
+        wait_vmcnt<0>();
+        lds_barrier();  // every wave's slices, score pieces and maxima have landed
+
+        // The reference scan over the round's tiles in key order (every wave of a key half
+        // computes the same values), then the weights of this wave's tiles (qv, qv + 4, qv + 8)
+        // against their references, written over their scores. Every LDS read goes out before
+        // the first use (a slot past the round's tiles is read and not used).
         constexpr int kMine = (kRing + 3) / 4;
-        float sk[kMine][8];
         f32x4 sraw[kMine][2];
 #pragma unroll
         for (int j = 0; j < kMine; j++) {
@@ -257,23 +403,10 @@ attn_split_values_kernel(AttnArgs a, int ntiles_max, int n_hg) {
             sraw[j][0] = sp[0];
             sraw[j][1] = sp[1];
         }
-#pragma unroll
-        for (int j = 0; j < kMine; j++) {
-            const int i = qv + 4 * j;
-            if (i < nt) {
-                const int t = t0 + i;
-                mloc_lds[kh][i][lane] = tile_scores(sraw[j][0], sraw[j][1], t * kTile + 32 * kh + 8 * g, n,
-                                                    (t + 1) * kTile <= n, scale2, sk[j]);
-            }
-        }
-        lds_barrier();
-        // Phase 2: the reference scan over the round's tiles in key order (every wave of a key
-        // half computes the same values), then the weights of this wave's tiles against their
-        // references, written over their scores.
         float ref_t[kRing], refp_t[kRing], mloc_t[kRing];
         uint32_t resc = 0;
 #pragma unroll
-        for (int i = 0; i < kRing; i++) mloc_t[i] = mloc_lds[kh][i][lane];
+        for (int i = 0; i < kRing; i++) mloc_t[i] = max_lds[i * 32 + kh * 16 + l16];
 #pragma unroll
         for (int i = 0; i < kRing; i++) {
             if (i < nt) {
@@ -293,8 +426,12 @@ attn_split_values_kernel(AttnArgs a, int ntiles_max, int n_hg) {
 #pragma unroll
                 for (int q = 1; q < 4; q++)
                     if (4 * j + q < kRing && qv == q) ref = ref_t[4 * j + q < kRing ? 4 * j + q : 0];
+                const int t = t0 + i;
+                float sk[8];
+                (void)tile_scores(sraw[j][0], sraw[j][1], t * kTile + 32 * kh + 8 * g, n, (t + 1) * kTile <= n, scale2,
+                                  sk);
                 bf16x8 ph, pl;
-                const float psum = tile_weights(sk[j], ref, ph, pl);
+                const float psum = tile_weights(sk, ref, ph, pl);
                 SA_LDS bf16x8 *pp = (SA_LDS bf16x8 *)lds_at<bf16x8>(s_base + i * kSTileB + (kh * 64 + lane) * 32);
                 pp[0] = ph;
                 pp[1] = pl;
@@ -302,8 +439,8 @@ attn_split_values_kernel(AttnArgs a, int ntiles_max, int n_hg) {
             }
         }
         lds_barrier();
-        // Phase 3: tile sums, rescales and value MFMAs in key order. The tile sums are read up
-        // front, and each tile's weights and value operand one tile ahead of its MFMAs.
+        // Tile sums, rescales and value MFMAs in key order. The tile sums are read up front, and
+        // each tile's weights and value operand one tile ahead of its MFMAs.
         float psum_t[kRing];
 #pragma unroll
         for (int i = 0; i < kRing; i++) psum_t[i] = psum_lds[kh][i][lane];
@@ -357,11 +494,32 @@ attn_split_values_kernel(AttnArgs a, int ntiles_max, int n_hg) {
         const f32x4 x1 = xch_lds[cq][lane];
         f32x4 o;
 #pragma unroll
-        for (int e = 0; e < 4; e++) o[e] = fold_elem(f, acc[0][e], x1[e], bad_mask);
+        for (int i = 0; i < 4; i++) o[i] = fold_elem(f, acc[0][i], x1[i], bad_mask);
         // Lane (g, l16): head 16hg + l16, columns cs*64 + 16cq + 4g + 0..3.
         float *dst = a.out + (row * a.H + head) * kHeadDim + cs * kSplitCols + 16 * cq + 4 * g;
         __builtin_nontemporal_store(o, (f32x4 *)dst);
     }
+    // The last consumer of the group advances E for the next launch on this workspace (every
+    // read of this launch's ready words is done by then).
+    if (w == 0 && lane == 0) {
+        const int hgs = n_hg - 4 * hb < 4 ? n_hg - 4 * hb : 4;
+        const uint64_t nv = (uint64_t)hgs * kSplitSlices;
+        const uint64_t old = __hip_atomic_fetch_add(sg + 1, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (old == nv - 1) __hip_atomic_store(sg, e + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+// Workgroups 0 .. n_prod-1 are producer tasks, n_prod .. n_prod_pad-1 idle, the others consumer
+// tasks.
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+attn_split_kernel(AttnArgs a, int ntiles_max, int n_hb, int n_hg, int64_t n_prod, int64_t n_prod_pad) {
+    __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
+    uint64_t *sync = (uint64_t *)a.ws;
+    const int64_t b = blockIdx.x;
+    if (b < n_prod_pad) {
+        if (b < n_prod) producer(a, lds, b, ntiles_max, n_hb, n_hg, sync);
+    } else
+        consumer(a, lds, xcd_remap(b - n_prod_pad, gridDim.x - n_prod_pad), ntiles_max, n_hb, n_hg, sync);
 }
 
 }  // namespace
@@ -370,20 +528,20 @@ hipError_t launch_attn_split(const AttnArgs &a, hipStream_t s) {
     const int ntiles_max = (a.kmax + kTile - 1) / kTile;
     const int n_hg = (a.H + 15) / 16;
     const int n_hb = (n_hg + 3) / 4;
-    const int64_t g1 = (int64_t)a.rows * ntiles_max * n_hb;
-    const int64_t g2 = (int64_t)a.rows * n_hg * kSplitSlices;
-    if (g1 == 0) return hipSuccess;
-    hipLaunchKernelGGL(attn_split_scores_kernel, dim3((unsigned)g1), dim3(512), 0, s, a, ntiles_max, n_hb, n_hg);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(attn_split_values_kernel, dim3((unsigned)g2), dim3(512), 0, s, a, ntiles_max, n_hg);
+    const int64_t n_prod = (int64_t)a.rows * ntiles_max * n_hb;
+    const int64_t n_cons = (int64_t)a.rows * n_hg * kSplitSlices;
+    if (n_prod == 0) return hipSuccess;
+    const int64_t n_prod_pad = (n_prod + 7) & ~(int64_t)7;
+    hipLaunchKernelGGL(attn_split_kernel, dim3((unsigned)(n_prod_pad + n_cons)), dim3(512), 0, s, a, ntiles_max, n_hb,
+                       n_hg, n_prod, n_prod_pad);
     return hipGetLastError();
 }
 
 size_t split_workspace_bytes(int64_t rows, int H, int32_t kmax) {
     const int64_t ntiles_max = (kmax + kTile - 1) / kTile;
     const int64_t n_hg = (H + 15) / 16;
-    return (size_t)(rows * ntiles_max * n_hg) * kSTileB;
+    if (rows <= 0) return 0;
+    return kSyncBytes + (size_t)(rows * ntiles_max * n_hg) * (kSTileB + kMTileB);
 }
 
 }  // namespace sa

@@ -46,10 +46,10 @@ hipError_t launch_unpad_heads(const float *out_pad, int64_t rows, int h_pad, int
                               hipStream_t s);
 
 // Launch geometry of the bf16 attention for a given problem. Small batches take the split
-// path (sa_attn_split.hip): the score contraction of every 64-key tile in its own workgroup,
-// the scores through the workspace, then the softmax and values per (row, 16-head group,
-// 64-column slice). Larger ones take the persistent kernels (sa_attn.hip). Both give the same
-// bits, so the choice is free to follow the batch size.
+// path (sa_attn_split.hip, one launch): the score contraction of every 64-key tile in its own
+// workgroup, the scores through the workspace, then the softmax and values per (row, 16-head
+// group, 64-column slice). Larger ones take the persistent kernels (sa_attn.hip). Both give
+// the same bits, so the choice is free to follow the batch size.
 struct AttnPlan {
     int split;              // 1: the split path
     int heads_per_wg;       // persistent kernels: 16, 32 or 64
@@ -61,12 +61,12 @@ struct AttnPlan {
     int lds_bytes_aliased;  // the same for one cache serving as both
     size_t ws_bytes;        // workspace the launch needs (0 for the persistent kernels)
 };
-// The split path takes rows whose index lists hold at most kSplitMaxK entries (the values
-// kernel keeps a row's list in LDS), when there are fewer than kSplitMaxUnits (row, 64-head
-// block) pairs: measured on the decode shape (64 heads, k = 640), the two split kernels take
-// 16 us at 1 row, 19 at 8 and 29 at 16 against 31-36 us for the persistent kernels, and break
-// even near 24 rows. This choice depends on the sizes only, never on the device, so that the
-// workspace a call needs does too.
+// The split path takes rows whose index lists hold at most kSplitMaxK entries (a consumer
+// workgroup keeps a row's list in LDS), when there are fewer than kSplitMaxUnits (row, 64-head
+// block) pairs: measured on the decode shape (64 heads, k = 640, back-to-back launches), it
+// takes 12 us at 1 row, 15 at 8, 23 at 16 and 35 at 23 against 31-38 us for the persistent
+// kernels, and breaks even near 24 rows. This choice depends on the sizes only, never on the
+// device, so that the workspace a call needs does too.
 constexpr int kSplitMaxK = 1024;
 constexpr int64_t kSplitMaxUnits = 24;
 AttnPlan plan_attn_bf16(int64_t rows, int H, int32_t kmax);

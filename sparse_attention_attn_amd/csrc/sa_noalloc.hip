@@ -7,8 +7,9 @@
 // device current, by hipGetSymbolAddress; only that address is ever passed to a kernel (the
 // array's name is a host-side stand-in on the host). Every call on one GPU shares the array, so
 // two calls in flight at once on one GPU (on different streams, or from different threads) race.
-// The kernels that use it (the bf16 and float32 split paths' score tiles) write every byte they
-// read in the same call, so nothing has to be cleared between calls.
+// The kernels that use it are the bf16 and float32 split paths. The float32 path writes every
+// byte it reads in the same call. The bf16 path also keeps sequence words there between calls,
+// and accepts any earlier contents for them, so nothing has to be cleared between calls.
 #include <hip/hip_runtime.h>
 
 #include <cstdio>

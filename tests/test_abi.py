@@ -49,6 +49,10 @@ def test_version_and_status_strings():
     assert lib.sparse_attn_status_string(99) == b"unknown status"
 
 
+SYNC = 24 * 32 * 8       # sync words: 32 of 8 bytes per (row, 64-head block), at most 24 pairs
+TILE = 4096 + 128        # one score tile and its maxima
+
+
 @pytest.mark.parametrize("op,rows,heads,kmax,expect", [
     # large batches: the persistent kernels, no workspace
     (L.SA_OP_DECODE, 1024, 64, 640, 0),
@@ -56,13 +60,14 @@ def test_version_and_status_strings():
     (L.SA_OP_DECODE, 24, 64, 640, 0),
     (L.SA_OP_DECODE, 12, 128, 640, 0),
     (L.SA_OP_PREFILL, 2048, 16, 640, 0),
-    # small batches: score tiles of 4 KiB per (row, 64-key tile, 16-head group)
-    (L.SA_OP_DECODE, 1, 64, 640, 1 * 10 * 4 * 4096),
-    (L.SA_OP_DECODE, 8, 64, 641, 8 * 11 * 4 * 4096),
-    (L.SA_OP_DECODE, 23, 64, 1, 23 * 1 * 4 * 4096),
-    (L.SA_OP_PREFILL, 11, 128, 64, 11 * 1 * 8 * 4096),
-    (L.SA_OP_DECODE, 2, 4, 64, 2 * 1 * 1 * 4096),
-    (L.SA_OP_DECODE, 2, 17, 1024, 2 * 16 * 2 * 4096),
+    # small batches: 6 KiB of sync words, then a 4 KiB score tile and 128 bytes of tile maxima
+    # per (row, 64-key tile, 16-head group)
+    (L.SA_OP_DECODE, 1, 64, 640, SYNC + 1 * 10 * 4 * TILE),
+    (L.SA_OP_DECODE, 8, 64, 641, SYNC + 8 * 11 * 4 * TILE),
+    (L.SA_OP_DECODE, 23, 64, 1, SYNC + 23 * 1 * 4 * TILE),
+    (L.SA_OP_PREFILL, 11, 128, 64, SYNC + 11 * 1 * 8 * TILE),
+    (L.SA_OP_DECODE, 2, 4, 64, SYNC + 2 * 1 * 1 * TILE),
+    (L.SA_OP_DECODE, 2, 17, 1024, SYNC + 2 * 16 * 2 * TILE),
     # index lists longer than 1,024 entries stay on the persistent kernels
     (L.SA_OP_DECODE, 1, 64, 1025, 0),
     # top-k and invalid sizes: none
@@ -97,10 +102,10 @@ def _decode(lib, **kw):
     (dict(kmax=0), L.SA_ERR_SHAPE),
     (dict(kmax=L.SA_MAX_KMAX + 1), L.SA_ERR_SHAPE),
     (dict(kmax=2 ** 31 - 1), L.SA_ERR_SHAPE),
-    (dict(rows=8, ws=A16, ws_bytes=8 * 10 * 4 * 4096 - 1), L.SA_ERR_WORKSPACE),
+    (dict(rows=8, ws=A16, ws_bytes=SYNC + 8 * 10 * 4 * TILE - 1), L.SA_ERR_WORKSPACE),
     (dict(rows=8), L.SA_ERR_WORKSPACE),
-    (dict(rows=8, ws=None, ws_bytes=8 * 10 * 4 * 4096), L.SA_ERR_NULL),
-    (dict(rows=8, ws=A16 + 8, ws_bytes=8 * 10 * 4 * 4096), L.SA_ERR_UNSUPPORTED),
+    (dict(rows=8, ws=None, ws_bytes=SYNC + 8 * 10 * 4 * TILE), L.SA_ERR_NULL),
+    (dict(rows=8, ws=A16 + 8, ws_bytes=SYNC + 8 * 10 * 4 * TILE), L.SA_ERR_UNSUPPORTED),
     (dict(n_ctx=0), L.SA_ERR_SHAPE),
     (dict(n_ctx=4194304), L.SA_ERR_UNSUPPORTED),  # bf16 caches: at most 2^22 - 1 positions
     (dict(dtype=L.SA_F32, n_ctx=2097152), L.SA_ERR_UNSUPPORTED),  # float32 caches: at most 2^21 - 1

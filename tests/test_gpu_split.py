@@ -1,6 +1,6 @@
-"""The split path for small batches (sa_attn_split.hip: scores of every 64-key tile in their own
-workgroup, then the softmax and values per head group and column slice) against the persistent
-kernels (sa_attn.hip) and the float64 oracle.
+"""The split path for small batches (sa_attn_split.hip, one launch: producer workgroups score
+every 64-key tile, consumer workgroups wait for a row's scores and run the softmax and values per
+head group and column slice) against the persistent kernels (sa_attn.hip) and the float64 oracle.
 
 A launch with fewer than 24 rows per block of 64 heads (and index lists of at most 1,024
 entries) takes the split path. The same rows padded with empty rows (nsel = 0, which read
@@ -107,7 +107,7 @@ def test_head_counts_ragged(heads):
 
 @pytest.mark.parametrize("k", [1, 63, 64, 65, 639, 640, 641, 704, 1023, 1024])
 def test_index_list_lengths(k):
-    """Tile boundaries and the values kernel's rounds (ten tiles per round: 641 and more take two)."""
+    """Tile boundaries and a consumer's rounds (ten tiles per round: 641 and more take two)."""
     c = w.decode_bf16(seed=300 + k, batch=2, heads=64, n_ctx=2000, k=k)
     check_both(c, f"k={k}")
 
@@ -213,6 +213,44 @@ def test_split_repeats_and_guards():
         outs.append(out.clone())
     for o in outs[1:]:
         assert torch.equal(o.view(torch.int32), outs[0].view(torch.int32))
+
+
+@pytest.mark.parametrize("fill", ["zeros", "0xAB", "random"])
+def test_workspace_contents_and_alternating_inputs(fill):
+    """The split path passes scores between workgroups of one launch through the workspace, with
+    per-tile ready words that depend on a sequence number the launch finds there. Whatever the
+    workspace held before (zeros, a repeated byte, random bytes, what launches of other shapes
+    left), every launch must wait for its own scores: calls that alternate between two input
+    sets, with launches of other shapes in between, on one workspace, must each return their
+    own inputs' result (a read of the previous call's scores would return the other set's)."""
+    sa, L = _lib()
+    shapes = [(3, 64, 2000, 640), (2, 128, 1500, 1000), (5, 16, 900, 700)]
+    need = max(sa.load().sparse_attn_workspace_bytes(L.SA_OP_DECODE, b, h, 512, k, n) for b, h, n, k in shapes)
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(333)
+    if fill == "zeros":
+        ws = torch.zeros((need,), dtype=torch.uint8, device=DEV)
+    elif fill == "0xAB":
+        ws = torch.full((need,), 0xAB, dtype=torch.uint8, device=DEV)
+    else:
+        ws = torch.randint(0, 256, (need,), generator=gen, dtype=torch.uint8, device=DEV)
+    sets = {}
+    for si, (b, h, n, k) in enumerate(shapes):
+        for v in range(2):
+            c = w.decode_bf16(seed=340 + 2 * si + v, batch=b, heads=h, n_ctx=n, k=k)
+            d = to_device(c, DEV)
+            # The reference: the same call with a workspace of its own (fresh allocation).
+            ref = sa.decode(d["q"], d["k"], d["v"], d["idx"], d["sinks"], c.scale, d["nsel"])
+            sets[(si, v)] = (c, d, ref)
+    torch.cuda.synchronize()
+    say(f"workspace {fill}: 3 shapes x 2 input sets, alternating on one workspace")
+    order = [(0, 0), (0, 1), (0, 0), (1, 0), (0, 1), (1, 1), (1, 0), (2, 0), (0, 0), (2, 1), (2, 0), (0, 1),
+             (1, 1), (0, 0), (0, 1), (0, 0)]
+    for i, key in enumerate(order):
+        c, d, ref = sets[key]
+        out = sa.decode(d["q"], d["k"], d["v"], d["idx"], d["sinks"], c.scale, d["nsel"], ws=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int32), ref.view(torch.int32)), f"call {i}: shape {key[0]} set {key[1]}"
 
 
 def test_workspace_too_small_is_refused_before_launch():
