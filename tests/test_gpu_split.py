@@ -253,6 +253,30 @@ def test_workspace_contents_and_alternating_inputs(fill):
         assert torch.equal(out.view(torch.int32), ref.view(torch.int32)), f"call {i}: shape {key[0]} set {key[1]}"
 
 
+def test_two_streams_at_once():
+    """Split launches in flight at once on two streams, each with its own workspace, inputs and
+    output (a consumer only ever waits for producers of its own launch): each call returns its own
+    result, over several rounds."""
+    sa, L = _lib()
+    cases = [w.decode_bf16(seed=350 + i, batch=b, heads=64, n_ctx=3000, k=640) for i, b in enumerate((2, 8))]
+    devs = [to_device(c, DEV) for c in cases]
+    refs = [sa.decode(d["q"], d["k"], d["v"], d["idx"], d["sinks"], c.scale, d["nsel"]) for c, d in zip(cases, devs)]
+    wss = [torch.empty((sa.load().sparse_attn_workspace_bytes(L.SA_OP_DECODE, c.rows, 64, 512, 640, 3000),),
+                       dtype=torch.uint8, device=DEV) for c in cases]
+    outs = [torch.empty_like(r) for r in refs]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(device=DEV) for _ in cases]
+    say("split path: two streams, 2 and 8 rows, 20 rounds")
+    for rnd in range(20):
+        for c, d, ws, o, st in zip(cases, devs, wss, outs, streams):
+            with torch.cuda.stream(st):
+                o.fill_(float("nan"))
+                sa.decode(d["q"], d["k"], d["v"], d["idx"], d["sinks"], c.scale, d["nsel"], out=o, ws=ws)
+        torch.cuda.synchronize()
+        for i, (o, r) in enumerate(zip(outs, refs)):
+            assert torch.equal(o.view(torch.int32), r.view(torch.int32)), f"round {rnd}: stream {i}"
+
+
 def test_workspace_too_small_is_refused_before_launch():
     sa, L = _lib()
     c = w.decode_bf16(seed=332, batch=2, heads=64, n_ctx=500, k=100)
