@@ -16,11 +16,13 @@
 // part. Here:
 //   1. attn_f32_split_scores_kernel: one workgroup per (row, tile, block of one, two or four
 //      16-head groups). Its eight waves gather the tile's 32 K rows once for the block and run
-//      attn_f32_kernel's score contraction for each head group (wave w: 16-key block w & 1 over
-//      dimension quarter w >> 1, the same MFMA steps on the same operands); wave i then sums
-//      head group i's quarters in order and stores the raw sums, in attn_f32_kernel's lane
-//      layout (lane (g, l16): tile keys g + 4e of head l16), to the workspace:
-//      [row][tile][16-head group][lane][8] fp32, 2 KiB per tile and head group.
+//      attn_f32_kernel's score contraction for each head group and 16-key block over each
+//      dimension quarter (the same MFMA steps on the same operands): wave w takes quarter
+//      w >> 1 and, with one head group, key block w & 1; with two or four, half of the head
+//      groups (w & 1) and both key blocks, so that no two waves load the same query columns.
+//      Wave i then sums head group i's quarters in order and stores the raw sums, in
+//      attn_f32_kernel's lane layout (lane (g, l16): tile keys g + 4e of head l16), to the
+//      workspace: [row][tile][16-head group][lane][8] fp32, 2 KiB per tile and head group.
 //   2. attn_f32_split_values_kernel: one workgroup per (row, 16-head group, 64-column slice),
 //      four waves, one 16-column block each, in rounds of up to twelve tiles. Each wave gathers
 //      its own columns of the round's V rows and loads the score sums of its share of the tiles;
@@ -79,7 +81,11 @@ attn_f32_split_scores_kernel(AttnArgs a, int ntiles_max, int n_hb, int n_hg) {
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int g = lane >> 4;
     const int l16 = lane & 15;
-    const int b_own = w & 1;
+    // One head group: wave w takes key block w & 1. Two or four: head groups HW (w & 1) .. +HW-1
+    // of the block (HW = HPB / 2) and both key blocks.
+    constexpr int HW = HPB == 1 ? 1 : HPB / 2;
+    constexpr int NB = HPB == 1 ? 1 : 2;
+    const int half = w & 1;
     const int dq = w >> 1;
     const int64_t bid = blockIdx.x;
     const int hb = (int)(bid % n_hb);
@@ -93,21 +99,23 @@ attn_f32_split_scores_kernel(AttnArgs a, int ntiles_max, int n_hb, int n_hg) {
     const int p = tile * kT32 + (lane & 31);
     float raw;
     load4_async(raw, a.idx + row * a.kmax + (p < a.kmax ? p : a.kmax - 1));
-    // Query of head group i for this wave's dimension quarter: lane (g, l16) holds dims
-    // 128 g + 32 dq .. +31 of head 16 (hg0 + i) + l16 (zero for heads past H).
-    float qv[HPB][32];
+    // Query of this wave's head group j (block head group jg) for its dimension quarter: lane
+    // (g, l16) holds dims 128 g + 32 dq .. +31 of head 16 (hg0 + jg) + l16 (zero for heads past H).
+    auto group_of = [&](int j) { return HPB == 1 ? 0 : HW * half + j; };
+    float qv[HW][32];
 #pragma unroll
-    for (int i = 0; i < HPB; i++) {
+    for (int j = 0; j < HW; j++) {
+        const int i = group_of(j);
         const int head = 16 * (hg0 + i) + l16;
         const bool ok = i < ng && head < a.H;
         const float *qrow = (const float *)a.q + (row * a.H + (ok ? head : 0)) * kHeadDim + 128 * g + 32 * dq;
 #pragma unroll
         for (int c = 0; c < 8; c++) {
             const f32x4 x = ok ? *(const f32x4 *)(qrow + 4 * c) : (f32x4){};
-            qv[i][4 * c] = x[0];
-            qv[i][4 * c + 1] = x[1];
-            qv[i][4 * c + 2] = x[2];
-            qv[i][4 * c + 3] = x[3];
+            qv[j][4 * c] = x[0];
+            qv[j][4 * c + 1] = x[1];
+            qv[j][4 * c + 2] = x[2];
+            qv[j][4 * c + 3] = x[3];
         }
     }
     const int n = row_count_f32(a, row);
@@ -135,24 +143,31 @@ attn_f32_split_scores_kernel(AttnArgs a, int ntiles_max, int n_hb, int n_hg) {
     wait_vmcnt<0>();
     lds_barrier();  // every wave's K rows have landed
 
-    // Partial scores of block b_own over the dimension quarter dq, for every head group of the
-    // block at once: four independent accumulation chains (a group past the heads contracts a
-    // zero query and is not stored), each in attn_f32_kernel's step order.
-    const SA_LDS char *krow = (const SA_LDS char *)k_lds + (16 * b_own + l16) * kKStrF + (128 * g + 32 * dq) * 4;
-    f32x4 sp[HPB] = {};
+    // Partial scores over the dimension quarter dq of this wave's (head group, key block) pairs:
+    // HW x NB independent accumulation chains (a group past the heads contracts a zero query and
+    // is not stored), each in attn_f32_kernel's step order.
+    const int b0 = HPB == 1 ? (w & 1) : 0;
+    const SA_LDS char *krow = (const SA_LDS char *)k_lds + (16 * b0 + l16) * kKStrF + (128 * g + 32 * dq) * 4;
+    f32x4 sp[HW][NB] = {};
 #pragma unroll
     for (int c = 0; c < 8; c++) {
-        const f32x4 kx = *(const SA_LDS f32x4 *)(krow + 16 * c);
+        f32x4 kx[NB];
+#pragma unroll
+        for (int bb = 0; bb < NB; bb++) kx[bb] = *(const SA_LDS f32x4 *)(krow + 16 * bb * kKStrF + 16 * c);
 #pragma unroll
         for (int e = 0; e < 4; e++) {
 #pragma unroll
-            for (int i = 0; i < HPB; i++)
-                sp[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(kx[e], qv[i][4 * c + e], sp[i], 0, 0, 0);
+            for (int j = 0; j < HW; j++)
+#pragma unroll
+                for (int bb = 0; bb < NB; bb++)
+                    sp[j][bb] = __builtin_amdgcn_mfma_f32_16x16x4f32(kx[bb][e], qv[j][4 * c + e], sp[j][bb], 0, 0, 0);
         }
     }
 #pragma unroll
-    for (int i = 0; i < HPB; i++)
-        if (i < ng) part_lds[i][dq][b_own][lane] = sp[i];
+    for (int j = 0; j < HW; j++)
+#pragma unroll
+        for (int bb = 0; bb < NB; bb++)
+            if (group_of(j) < ng) part_lds[group_of(j)][dq][b0 + bb][lane] = sp[j][bb];
     lds_barrier();  // every head group's partials are in LDS
 
     // Wave i sums head group i's four quarters in order and stores the raw sums.
