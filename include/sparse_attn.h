@@ -107,7 +107,9 @@ const char *sparse_attn_last_error(void);
  * rows x ceil(kmax / 64) x ceil(heads / 16) x 4,224 bytes. Larger batches need no
  * workspace. A row's result is the same, bit for bit, on either path (the ds4
  * commit log for ds4_tp.c: a split that follows the launch must not change the
- * output bytes).
+ * output bytes). On the bf16 split path a workgroup that waits more than 200 ms
+ * for its row's scores (a device held by other work beyond any normal load) stops
+ * waiting and writes its part of the row as NaN, so a call always completes.
  * Float32 launches with fewer than 17 rows per block of 64 heads and index lists
  * of 129 to 1,024 entries split the same way, with 32-key tiles of 2 KiB (rows x
  * ceil(kmax / 32) x ceil(heads / 16) x 2 KiB, never more than the bf16 figure).
