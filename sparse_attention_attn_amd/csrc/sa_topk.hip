@@ -14,8 +14,9 @@
 //     in registers; T is found by three radix passes from the top (11, 11 and 10
 //     bits), each an LDS histogram of the keys that share the digits found so far
 //     and one scan that locates the digit where the count from the top reaches k.
-//     A row takes 4 or 8 waves (topk_rows8_kernel: 8 waves and 8 keys per lane, held to
-//     eight waves per SIMD so that four rows share a CU).
+//     A row takes 4, 8 or 16 waves (topk_rows8_kernel: 8 waves and 8 keys per lane, held to
+//     eight waves per SIMD so that four rows share a CU; 16 waves for rows of more than 4,096
+//     scores when there is at most one row per CU).
 //   * topk_radix_kernel (longer rows): four 8-bit radix passes with LDS
 //     histograms, the keys cached in LDS when the row fits (32,768 scores) and
 //     re-read from memory otherwise.
@@ -183,7 +184,8 @@ __device__ __forceinline__ void topk_regs_row(TopkArgs a) {
     constexpr int kWaveSpan = 64 * KPL;
     constexpr int kBins = 2048;
     constexpr int kBinsPerThread = kBins / (64 * WAVES);
-    static_assert(kBinsPerThread % 4 == 0, "bins are read and cleared 16 bytes at a time");
+    constexpr int kVW = kBinsPerThread >= 4 ? 4 : kBinsPerThread;  // bins per LDS access
+    static_assert(kVW >= 2 && kBinsPerThread % kVW == 0, "bins are read and cleared 8 or 16 bytes at a time");
     __shared__ uint32_t cnt_lds[2][WAVES];
     __shared__ __attribute__((aligned(16))) uint32_t hist[kBins];
     __shared__ uint32_t pick_lds[4];  // digit, count above it, count in it; T (early exit)
@@ -224,10 +226,10 @@ __device__ __forceinline__ void topk_regs_row(TopkArgs a) {
     for (int r = 0; r < KPL; r++) key[r] = order_key(x[r]) & live(base + 64 * r);
 
     // ---- radix passes. hist starts at zero and every thread clears the bins it read.
-    typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
-    u32x4v *hv = (u32x4v *)&hist[threadIdx.x * kBinsPerThread];
+    typedef uint32_t binv __attribute__((ext_vector_type(kVW)));
+    binv *hv = (binv *)&hist[threadIdx.x * kBinsPerThread];
 #pragma unroll
-    for (int i = 0; i < kBinsPerThread / 4; i++) hv[i] = (u32x4v){0u, 0u, 0u, 0u};
+    for (int i = 0; i < kBinsPerThread / kVW; i++) hv[i] = (binv){};
     uint32_t prefix = 0u, krem = k, t_count = 0u;
 #pragma unroll
     for (int pass = 0; pass < 3; pass++) {
@@ -244,12 +246,12 @@ __device__ __forceinline__ void topk_regs_row(TopkArgs a) {
         uint32_t h[kBinsPerThread];
         uint32_t mine = 0u;
 #pragma unroll
-        for (int i = 0; i < kBinsPerThread / 4; i++) {
-            const u32x4v v = hv[i];
-            hv[i] = (u32x4v){0u, 0u, 0u, 0u};
+        for (int i = 0; i < kBinsPerThread / kVW; i++) {
+            const binv v = hv[i];
+            hv[i] = (binv){};
 #pragma unroll
-            for (int e = 0; e < 4; e++) {
-                h[4 * i + e] = v[e];
+            for (int e = 0; e < kVW; e++) {
+                h[kVW * i + e] = v[e];
                 mine += v[e];
             }
         }
@@ -398,15 +400,22 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(8, 8))
 hipError_t launch_topk(const TopkArgs &a, hipStream_t s) {
     if (a.rows == 0) return hipSuccess;
     const dim3 grid((unsigned)a.rows);
+    const int64_t cus = device_cu_count();
     if (a.n <= 64 * 64) {
         // With at most four rows per CU, eight waves per row shorten each row's chain;
         // beyond that, four waves per row keep more rows in flight.
-        if (a.rows <= 4 * (int64_t)device_cu_count())
+        if (a.rows <= 4 * cus)
             hipLaunchKernelGGL(topk_rows8_kernel, grid, dim3(512), 0, s, a);
         else
             hipLaunchKernelGGL((topk_regs_kernel<4, 16>), grid, dim3(256), 0, s, a);
+    } else if (a.n <= 16 * 64 * 16 && a.rows <= cus) {
+        // At most one row per CU: sixteen waves per row, 16 or 32 keys per lane, shorten each
+        // row's chain (8 x 16,384: 18.4 -> 9.9 us; 8 x 32,768: 20.3 -> 17.5 us, measured).
+        hipLaunchKernelGGL((topk_regs_kernel<16, 16>), grid, dim3(1024), 0, s, a);
     } else if (a.n <= 4 * 64 * 64) {
         hipLaunchKernelGGL((topk_regs_kernel<4, 64>), grid, dim3(256), 0, s, a);
+    } else if (a.n <= 16 * 64 * 32 && a.rows <= cus) {
+        hipLaunchKernelGGL((topk_regs_kernel<16, 32>), grid, dim3(1024), 0, s, a);
     } else if (a.n <= 8 * 64 * 64) {
         hipLaunchKernelGGL((topk_regs_kernel<8, 64>), grid, dim3(512), 0, s, a);
     } else {

@@ -1,6 +1,7 @@
 """Seeded random top-k cases, bit-exact against the oracle, across every launch shape: rows of
 up to 4,096 (eight-wave rows when there are at most four rows per CU, four-wave rows beyond),
-up to 16,384 and 32,768 (register kernels) and longer (the radix kernel); k below and above the
+up to 16,384 and 32,768 (register kernels: sixteen waves per row when there is at most one row
+per CU) and longer (the radix kernel); k below and above the
 valid length; per-row valid lengths; N(0,1) scores, scores rounded to a coarse grid (many ties
 at the threshold), and rows with planted +-0, NaN and +-inf.
 """
@@ -25,9 +26,12 @@ def random_topk_case(seed: int):
     rng = np.random.default_rng(20_000 + seed)
     n = int(rng.choice([1, 63, 64, 65, 640, 4096, 4097, 16384, 16385, 32768, 40000, int(rng.integers(2, 5000))]))
     rows = int(rng.choice([1, 3, 37, 1024, 1025, 2048])) if n <= 4096 else int(rng.integers(1, 40))
-    # The first seeds pin the launch-shape boundaries: the radix kernel (rows past 32,768),
-    # and at most vs more than four rows per CU (eight-wave vs four-wave rows).
-    n, rows = {0: (40000, 5), 1: (4096, 1024), 2: (4096, 1025), 3: (32769, 3)}.get(seed, (n, rows))
+    # The first seeds pin the launch-shape boundaries: the radix kernel (rows past 32,768), at
+    # most vs more than four rows per CU (eight-wave vs four-wave rows) for rows of up to 4,096,
+    # and at most vs more than one row per CU (sixteen-wave rows vs four- or eight-wave rows) for
+    # rows of up to 16,384 and 32,768.
+    n, rows = {0: (40000, 5), 1: (4096, 1024), 2: (4096, 1025), 3: (32769, 3), 4: (16384, 300),
+               5: (32768, 257), 6: (16385, 256), 7: (4097, 2)}.get(seed, (n, rows))
     k = int(rng.choice([1, 2, 64, 640, 2048, int(rng.integers(1, n + 2))]))
     ld = n + int(rng.choice([0, 0, 3]))
     s = rng.standard_normal((rows, ld)).astype(np.float32)
