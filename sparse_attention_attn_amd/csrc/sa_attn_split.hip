@@ -14,12 +14,14 @@
 // kernels one workgroup walks them in a chain, each tile waiting twice for rows gathered from
 // HBM, so a launch of one or a few rows takes about 30 us whatever the chip's size. Here every
 // workgroup of attn_split_kernel takes one or two roles:
-//   * producer of (row, tile, block of 64 heads): its eight waves gather the tile's 64 K rows
-//     once and run the score MFMA chain exactly as the persistent kernel does (same wave roles:
-//     key half kh = w >> 2, 16-head group w & 3; same K slot order and operand layout). The
-//     block's query goes through LDS once (64 KiB, one DMA per head). It stores each wave's raw
-//     scores, in its lane layout, and each key half's tile maximum per head, then publishes the
-//     tile's ready word.
+//   * producer of (row, tile, block of 16 HPB heads, HPB = 1, 2 or 4): its eight waves gather
+//     the tile's 64 K rows once, and 2 HPB of them run the score MFMA chain exactly as the
+//     persistent kernel does (one key half and one 16-head group each; same K slot order and
+//     operand layout). The block's query goes through LDS once (one 1 KiB DMA per head). It
+//     stores each scoring wave's raw scores, in its lane layout, and each key half's tile
+//     maximum per head, then publishes the tile's ready word. A narrower block puts each score
+//     chain on a SIMD of its own, and the launch takes the narrowest that still fits the chip in
+//     one round of workgroups (one row: 16 heads, 10.6 against 12.5 us for 64).
 //   * consumer of (row, 16-head group, 64-column slice): it loads the row's index list and
 //     gathers the V column slices of a round of up to ten tiles while the producers run, waits
 //     for the ready words of the row's tiles, loads their scores and maxima, then runs, per wave
@@ -38,7 +40,7 @@
 // so that eight decode rows need 266 workgroups instead of 336, measured slower: 15.9 against
 // 14.5 us; without the XCD remap, eight rows took 16.1 us.)
 //
-// Synchronisation through the workspace. Its first kSyncBytes hold, per (row, 64-head block),
+// Synchronisation through the workspace. Its first kSyncBytes hold, per (row, producer block),
 // a sequence number E, a consumer count U and one ready word per tile. Every workgroup reads E
 // at its start; a producer stores its scores and maxima with device-scope (sc1) stores, waits
 // until they have completed, and then stores the ready word ready_word(E, tile); a consumer
@@ -69,7 +71,7 @@ constexpr int kRing = 10;                      // tiles per round of a consumer
 constexpr int kMaxTiles = kSplitMaxK / kTile;
 static_assert(kSplitCols == 64 && kVRowB == 128, "a consumer's waves own 16 columns each");
 
-// Sync words: 32 per (row, 64-head block): [0] E, [1] U, [2 + t] the ready word of tile t.
+// Sync words: 32 per (row, producer block): [0] E, [1] U, [2 + t] the ready word of tile t.
 constexpr int kSyncGroupWords = 32;
 constexpr size_t kSyncBytes = (size_t)kSplitMaxUnits * kSyncGroupWords * 8;
 static_assert(2 + kMaxTiles <= kSyncGroupWords, "the ready words fit a group");
@@ -134,7 +136,8 @@ constexpr int kLdsProducer = kOffQ + 64 * kRowBytes;
 constexpr int kLdsBytes = kLdsConsumer > kLdsProducer ? kLdsConsumer : kLdsProducer;
 static_assert(kLdsBytes <= 160 * 1024, "LDS of one workgroup");
 
-// Producer task b of the launch: (row, tile, head block), head blocks fastest.
+// Producer task b of the launch: (row, tile, head block of 16 HPB heads), head blocks fastest.
+template <int HPB>
 __device__ __forceinline__ void producer(const AttnArgs &a, char *lds, int64_t b, int ntiles_max, int n_hb, int n_hg,
                                          uint64_t *sync) {
     char *k_lds = lds;
@@ -144,16 +147,18 @@ __device__ __forceinline__ void producer(const AttnArgs &a, char *lds, int64_t b
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int g = lane >> 4;
     const int l16 = lane & 15;
-    const int wi = w & 3;
-    const int kh = w >> 2;
+    // Score roles: wave w < 2 HPB takes key half kh = w / HPB and head group wi = w % HPB of
+    // the block; gather roles: wave w gathers tile keys 8w .. 8w+7.
+    const int wi = w % HPB;
+    const int kh = w / HPB;
     const int hb = (int)(b % n_hb);
     const int tile = (int)((b / n_hb) % ntiles_max);
     const int64_t row = b / ((int64_t)n_hb * ntiles_max);
-    const int hg = 4 * hb + wi;
+    const int hg = HPB * hb + wi;
     uint64_t *sg = sync + (row * n_hb + hb) * kSyncGroupWords;
 
     // First memory round trip: E, the tile's index list and the row's count; the block's query
-    // follows (64 heads x 1 KiB into LDS, wave w moving heads 8w .. 8w+7) and may still be in
+    // follows (16 HPB heads x 1 KiB into LDS, 2 HPB per wave) and may still be in
     // flight while the K rows are gathered. Head h's row is stored rotated by h chunks of 16
     // bytes, so that 16 heads read at one column hit 16 different bank groups.
     const uint64_t e = __hip_atomic_load(sg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -163,15 +168,15 @@ __device__ __forceinline__ void producer(const AttnArgs &a, char *lds, int64_t b
         dma4(a.idx + row * a.kmax, (uint32_t)pc * 4u, lds_addr(&idx_lds[w][0]));
     }
 #pragma unroll
-    for (int i = 0; i < 8; i++) {
-        const int hl = 8 * w + i;
-        const int h = 64 * hb + hl;
+    for (int i = 0; i < 2 * HPB; i++) {
+        const int hl = 2 * HPB * w + i;
+        const int h = 16 * HPB * hb + hl;
         const void *src = h < a.H ? (const void *)((const uint16_t *)a.q + (row * a.H + h) * kHeadDim)
                                   : (const void *)g_zero_row;
         dma16(src, (uint32_t)((lane - hl) & 63) << 4, lds_addr(q_lds + hl * kRowBytes));
     }
     const int n = row_count(a, row);
-    wait_vmcnt<8>();  // E and the index list; the query's eight rows may still be in flight
+    wait_vmcnt<2 * HPB>();  // E and the index list; the query's rows may still be in flight
     // Tiles past the row's count have no selected key and no consumer waits for them; tile 0
     // always publishes (its producer resets the group's consumer count).
     const int nwait = n > 0 ? (n + kTile - 1) / kTile : 1;
@@ -186,15 +191,15 @@ __device__ __forceinline__ void producer(const AttnArgs &a, char *lds, int64_t b
         const int iv_raw = idx_lds[w][lane];
         const bool live = tile * kTile + lane < n;
         const int iv = (live && iv_raw >= 0 && (int64_t)iv_raw < a.n_ctx) ? iv_raw : -1;
-        // Wave w gathers tile keys 8w .. 8w+7 (its key half) into the K slots of the persistent
-        // kernels: key 32kh + kap goes to slot 32kh + kslot_of_key(kap).
+        // Wave w gathers tile keys 8w .. 8w+7 (key half w >> 2) into the K slots of the
+        // persistent kernels: key 32kh + kap goes to slot 32kh + kslot_of_key(kap).
         const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
             (void *)((const char *)a.k + row * a.cache_stride * 2), 0, (int)(uint32_t)(a.n_ctx * kRowBytes),
             kBufferFlags);
 #pragma unroll
         for (int i = 0; i < kRows; i++) {
             const int ij = __builtin_amdgcn_readlane(iv, kRows * w + i);
-            const int slot = 32 * kh + kslot_of_key(8 * wi + i);
+            const int slot = 32 * (w >> 2) + kslot_of_key(8 * (w & 3) + i);
             dma16_buf(rk, ((uint32_t)ij << 10) + ((uint32_t)lane << 4),
                       lds_addr((SA_LDS char *)k_lds + slot * kKStride));
         }
@@ -209,7 +214,7 @@ __device__ __forceinline__ void producer(const AttnArgs &a, char *lds, int64_t b
         }
         wait_vmcnt<0>();
         lds_barrier();  // every wave's K rows have landed
-        if (hg < n_hg) {
+        if (kh < 2 && hg < n_hg) {
             const SA_LDS char *krow = (const SA_LDS char *)k_lds + (32 * kh + l16) * kKStride + 16 * g;
             f32x4 sacc0, sacc1;
             score_chain(krow, qreg, sacc0, sacc1, [](int) {});
@@ -249,6 +254,7 @@ __device__ __forceinline__ void producer(const AttnArgs &a, char *lds, int64_t b
 // .. +15 (one MFMA block). The four waves of a key half split a round's tiles for the
 // expensive part of the online softmax (scaled scores, weights), share the weights through
 // LDS, and each runs the cheap sequential parts (reference scan, tile sums) itself.
+template <int HPB>
 __device__ __forceinline__ void consumer(const AttnArgs &a, char *lds, int64_t u, int ntiles_max, int n_hb, int n_hg,
                                          uint64_t *sync) {
     char *v_lds = lds + kOffV;
@@ -273,7 +279,7 @@ __device__ __forceinline__ void consumer(const AttnArgs &a, char *lds, int64_t u
     const int hg = (int)((u / kSplitSlices) % n_hg);
     const int64_t row = u / ((int64_t)kSplitSlices * n_hg);
     const int head = 16 * hg + l16;
-    const int hb = hg >> 2;
+    const int hb = hg / HPB;
     uint64_t *sg = sync + (row * n_hb + hb) * kSyncGroupWords;
 
     // First memory round trip: E, the row's index list (the first ntiles_max * 64 entries, the
@@ -502,7 +508,7 @@ __device__ __forceinline__ void consumer(const AttnArgs &a, char *lds, int64_t u
     // The last consumer of the group advances E for the next launch on this workspace (every
     // read of this launch's ready words is done by then).
     if (w == 0 && lane == 0) {
-        const int hgs = n_hg - 4 * hb < 4 ? n_hg - 4 * hb : 4;
+        const int hgs = n_hg - HPB * hb < HPB ? n_hg - HPB * hb : HPB;
         const uint64_t nv = (uint64_t)hgs * kSplitSlices;
         const uint64_t old = __hip_atomic_fetch_add(sg + 1, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (old == nv - 1) __hip_atomic_store(sg, e + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -511,15 +517,16 @@ __device__ __forceinline__ void consumer(const AttnArgs &a, char *lds, int64_t u
 
 // Workgroups 0 .. n_prod-1 are producer tasks, n_prod .. n_prod_pad-1 idle, the others consumer
 // tasks.
+template <int HPB>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_split_kernel(AttnArgs a, int ntiles_max, int n_hb, int n_hg, int64_t n_prod, int64_t n_prod_pad) {
     __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
     uint64_t *sync = (uint64_t *)a.ws;
     const int64_t b = blockIdx.x;
     if (b < n_prod_pad) {
-        if (b < n_prod) producer(a, lds, b, ntiles_max, n_hb, n_hg, sync);
+        if (b < n_prod) producer<HPB>(a, lds, b, ntiles_max, n_hb, n_hg, sync);
     } else
-        consumer(a, lds, xcd_remap(b - n_prod_pad, gridDim.x - n_prod_pad), ntiles_max, n_hb, n_hg, sync);
+        consumer<HPB>(a, lds, xcd_remap(b - n_prod_pad, gridDim.x - n_prod_pad), ntiles_max, n_hb, n_hg, sync);
 }
 
 }  // namespace
@@ -527,13 +534,29 @@ attn_split_kernel(AttnArgs a, int ntiles_max, int n_hb, int n_hg, int64_t n_prod
 hipError_t launch_attn_split(const AttnArgs &a, hipStream_t s) {
     const int ntiles_max = (a.kmax + kTile - 1) / kTile;
     const int n_hg = (a.H + 15) / 16;
-    const int n_hb = (n_hg + 3) / 4;
-    const int64_t n_prod = (int64_t)a.rows * ntiles_max * n_hb;
     const int64_t n_cons = (int64_t)a.rows * n_hg * kSplitSlices;
-    if (n_prod == 0) return hipSuccess;
+    if (a.rows <= 0 || ntiles_max == 0) return hipSuccess;
+    // Producer blocks of 16, 32 or 64 heads: the narrowest whose launch fits the chip in one
+    // round of workgroups (a narrower block runs its score chains on fewer SIMDs at once).
+    const int64_t cus = device_cu_count();
+    int hpb = 4;
+    for (int c = 1; c < 4; c *= 2) {
+        const int64_t nhb = (n_hg + c - 1) / c;
+        if (a.rows * nhb < kSplitMaxUnits && a.rows * ntiles_max * nhb + n_cons <= cus) {
+            hpb = c;
+            break;
+        }
+    }
+    const int n_hb = (n_hg + hpb - 1) / hpb;
+    const int64_t n_prod = (int64_t)a.rows * ntiles_max * n_hb;
     const int64_t n_prod_pad = (n_prod + 7) & ~(int64_t)7;
-    hipLaunchKernelGGL(attn_split_kernel, dim3((unsigned)(n_prod_pad + n_cons)), dim3(512), 0, s, a, ntiles_max, n_hb,
-                       n_hg, n_prod, n_prod_pad);
+    const dim3 grid((unsigned)(n_prod_pad + n_cons));
+    if (hpb == 1)
+        hipLaunchKernelGGL(attn_split_kernel<1>, grid, dim3(512), 0, s, a, ntiles_max, n_hb, n_hg, n_prod, n_prod_pad);
+    else if (hpb == 2)
+        hipLaunchKernelGGL(attn_split_kernel<2>, grid, dim3(512), 0, s, a, ntiles_max, n_hb, n_hg, n_prod, n_prod_pad);
+    else
+        hipLaunchKernelGGL(attn_split_kernel<4>, grid, dim3(512), 0, s, a, ntiles_max, n_hb, n_hg, n_prod, n_prod_pad);
     return hipGetLastError();
 }
 

@@ -64,7 +64,7 @@ struct AttnPlan {
 // The split path takes rows whose index lists hold at most kSplitMaxK entries (a consumer
 // workgroup keeps a row's list in LDS), when there are fewer than kSplitMaxUnits (row, 64-head
 // block) pairs: measured on the decode shape (64 heads, k = 640, back-to-back launches), it
-// takes 12 us at 1 row, 15 at 8, 23 at 16 and 35 at 23 against 31-38 us for the persistent
+// takes 11 us at 1 row, 15 at 8, 23 at 16 and 35 at 23 against 31-38 us for the persistent
 // kernels, and breaks even near 24 rows. This choice depends on the sizes only, never on the
 // device, so that the workspace a call needs does too.
 constexpr int kSplitMaxK = 1024;

@@ -94,6 +94,17 @@ def test_decode_single_row_k640():
     check_both(w.decode_bf16(), "decode 1 row")
 
 
+@pytest.mark.parametrize("batch", [1, 3, 4, 5, 7])
+def test_producer_block_widths(batch):
+    """The decode shape at 1 to 7 rows: on a 256-CU part the launch scores with blocks of 16
+    heads (1 and 3 rows), 32 heads (4 rows) and 64 heads (5 and 7 rows); every width gives the
+    persistent kernels' bits."""
+    c = w.decode_bf16(seed=400 + batch, batch=batch, heads=64, n_ctx=3000, k=640)
+    c.nsel[-1] = 333
+    c.idx[-1, 333:] = -1
+    check_both(c, f"producer blocks, {batch} rows", oracle_rows=[0, batch - 1])
+
+
 @pytest.mark.parametrize("heads", [1, 4, 16, 17, 32, 48, 64, 100, 128])
 def test_head_counts_ragged(heads):
     """Head counts off the 16-head groups, with a full, an empty and a partial row (a masked tail)."""
