@@ -45,9 +45,10 @@
 // at its start; a producer stores its scores and maxima with device-scope (sc1) stores, waits
 // until they have completed, and then stores the ready word ready_word(E, tile); a consumer
 // polls the ready words of its row's tiles with device-scope loads until all match, then reads
-// the scores with device-scope loads. The producer of tile 0 first resets U; the last consumer
-// of the group (the one that brings U to the group's consumer count) stores E + 1 after all its
-// reads, so the next launch on this workspace waits for different words. The words are mixed
+// the scores with device-scope loads. The producer of tile 0 first resets U; every consumer adds
+// one to U once its reads of sync words are done (the add's round trip runs beside the value
+// products), and the one that brings U to the group's consumer count stores E + 1 at its end,
+// so the next launch on this workspace waits for different words. The words are mixed
 // with the tile index, so that no earlier contents of the workspace (zeros, a repeated byte,
 // data of another launch shape) can pass for a ready word except by a 64-bit coincidence.
 #include <hip/hip_runtime.h>
@@ -103,28 +104,22 @@ __device__ __forceinline__ int row_count(const AttnArgs &a, int64_t row) {
     return n < 0 ? 0 : (n > a.kmax ? a.kmax : n);
 }
 
+constexpr int kStoreDevice = 16;   // cache policy sc1 of a buffer load or store: device scope
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-// Direct-to-LDS load of 4 bytes per lane at device scope (sc1: it reads what another
-// workgroup's device-scope stores left, never a stale cached copy), from sbase + voff_i to LDS
-// address lds + 4 i. sbase is taken from the first active lane.
-__device__ __forceinline__ void dma4_device(const void *sbase, uint32_t voff, uint32_t lds) {
-    const uint64_t p = (uint64_t)(uintptr_t)sbase;
-    const uint64_t pu = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)p) |
-                        ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(p >> 32)) << 32);
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2 sc1"
-                 ::"s"(lds), "v"(voff), "s"(pu) : "memory", "m0");
+// Device-scope atomic add returning the old value asynchronously: old may be used only after
+// an explicit vector-memory wait that covers it, followed by register_ready.
+__device__ __forceinline__ void atomic_add_async(uint64_t &old, uint64_t *p, uint64_t v) {
+    asm volatile("global_atomic_add_x2 %0, %1, %2, off sc0" : "=v"(old) : "v"(p), "v"(v) : "memory");
 }
 #pragma clang diagnostic pop
-constexpr int kStoreDevice = 16;   // cache policy sc1 of a buffer store: device scope
 
 // LDS of the two roles, one array (a workgroup takes one role).
-// Consumer: V ring, score/weight ring, maxima, tile sums, index list, fold metadata, the fold
-// exchange, bad-index flags. Producer: K tile, index lists, the block's query.
+// Consumer: V ring, weight ring, tile sums, index list, fold metadata, the fold exchange,
+// bad-index flags. Producer: K tile, index lists, the block's query.
 constexpr int kOffV = 0;
 constexpr int kOffS = kOffV + kRing * kVTileB;
-constexpr int kOffMax = kOffS + kRing * kSTileB;
-constexpr int kOffPsum = kOffMax + kRing * kMTileB;
+constexpr int kOffPsum = kOffS + kRing * kSTileB;
 constexpr int kOffIdx = kOffPsum + 2 * kRing * 64 * 4;
 constexpr int kOffMeta = kOffIdx + kSplitMaxK * 4;
 constexpr int kOffXch = kOffMeta + 4 * 3 * 16 * 4;
@@ -259,7 +254,6 @@ __device__ __forceinline__ void consumer(const AttnArgs &a, char *lds, int64_t u
                                          uint64_t *sync) {
     char *v_lds = lds + kOffV;
     char *s_lds = lds + kOffS;
-    const float *max_lds = (const float *)(lds + kOffMax);   // [tile][key half][head]
     float (*psum_lds)[kRing][64] = (float (*)[kRing][64])(lds + kOffPsum);
     int *idx_lds = (int *)(lds + kOffIdx);
     float (*meta_lds)[3][16] = (float (*)[3][16])(lds + kOffMeta);
@@ -376,43 +370,43 @@ __device__ __forceinline__ void consumer(const AttnArgs &a, char *lds, int64_t u
     }
     lds_barrier();
 
+    // This consumer's count for the group (U): the one that brings it to the group's consumer
+    // count advances E at its end. It goes out once every read of sync words is done, at a
+    // point where no later wait covers it until the end.
+    const int hgs = n_hg - HPB * hb < HPB ? n_hg - HPB * hb : HPB;
+    const uint64_t nv = (uint64_t)hgs * kSplitSlices;
+    uint64_t u_old = 0;
+    if (ntiles == 0 && w == 0 && lane == 0) atomic_add_async(u_old, sg + 1, 1);
     for (int t0 = 0; t0 < ntiles; t0 += kRing) {
         const int nt = ntiles - t0 < kRing ? ntiles - t0 : kRing;
         if (t0 > 0) issue_v(t0, nt);
-        // The round's score tiles (each wave moves 512 bytes of every 4 KiB tile, in two
-        // 256-byte pieces) and maxima (wave w moves tiles w and w + 8), at device scope.
-        for (int i = 0; i < nt; i++) {
-            const uint32_t off = (uint32_t)(t0 + i) * (uint32_t)(n_hg * kSTileB) + 512u * w + 4u * lane;
-            dma4_device(sws, off, s_base + i * kSTileB + 512 * w);
-            dma4_device(sws, off + 256u, s_base + i * kSTileB + 512 * w + 256);
-        }
-#pragma unroll
-        for (int r = 0; r < 2; r++) {
-            const int i = w + 8 * r;
-            if (i < nt && lane < 32)
-                dma4_device(mws, (uint32_t)((t0 + i) * n_hg * kMTileB + 4 * lane),
-                            lds_addr((const char *)max_lds + i * kMTileB));
-        }
-        wait_vmcnt<0>();
-        lds_barrier();  // every wave's slices, score pieces and maxima have landed
-
-        // The reference scan over the round's tiles in key order (every wave of a key half
-        // computes the same values), then the weights of this wave's tiles (qv, qv + 4, qv + 8)
-        // against their references, written over their scores. Every LDS read goes out before
-        // the first use (a slot past the round's tiles is read and not used).
+        // This wave's tiles' scores (qv, qv + 4, qv + 8) and every tile's maxima of its key half,
+        // by device-scope loads straight into registers (a slot past the round's tiles reloads
+        // its last tile and is not used).
         constexpr int kMine = (kRing + 3) / 4;
+        const __amdgpu_buffer_rsrc_t rsc = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)sws, 0, ((ntiles_max - 1) * n_hg + 1) * kSTileB, kBufferFlags);
+        const __amdgpu_buffer_rsrc_t rmx = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)mws, 0, ((ntiles_max - 1) * n_hg + 1) * kMTileB, kBufferFlags);
         f32x4 sraw[kMine][2];
 #pragma unroll
         for (int j = 0; j < kMine; j++) {
-            const int i = qv + 4 * j < kRing ? qv + 4 * j : kRing - 1;
-            const SA_LDS f32x4 *sp = lds_at<f32x4>(s_base + i * kSTileB + (kh * 64 + lane) * 32);
-            sraw[j][0] = sp[0];
-            sraw[j][1] = sp[1];
+            const int i = qv + 4 * j < nt ? qv + 4 * j : nt - 1;
+            const int off = (t0 + i) * n_hg * kSTileB + (kh * 64 + lane) * 32;
+            sraw[j][0] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rsc, off, 0, kStoreDevice));
+            sraw[j][1] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rsc, off + 16, 0, kStoreDevice));
         }
         float ref_t[kRing], refp_t[kRing], mloc_t[kRing];
         uint32_t resc = 0;
 #pragma unroll
-        for (int i = 0; i < kRing; i++) mloc_t[i] = max_lds[i * 32 + kh * 16 + l16];
+        for (int i = 0; i < kRing; i++) {
+            const int ic = i < nt ? i : nt - 1;
+            mloc_t[i] = __uint_as_float(
+                __builtin_amdgcn_raw_buffer_load_b32(rmx, (t0 + ic) * n_hg * kMTileB + (kh * 16 + l16) * 4, 0, kStoreDevice));
+        }
+        // The reference scan over the round's tiles in key order (every wave of a key half
+        // computes the same values), then the weights of this wave's tiles against their
+        // references, into the weight ring.
 #pragma unroll
         for (int i = 0; i < kRing; i++) {
             if (i < nt) {
@@ -444,6 +438,14 @@ __device__ __forceinline__ void consumer(const AttnArgs &a, char *lds, int64_t u
                 psum_lds[kh][i][lane] = psum;
             }
         }
+        // Every register load of the round counts as used here, so that the compiler has no load
+        // of its own in flight past this point (its next wait would cover the count below).
+#pragma unroll
+        for (int i = 0; i < kRing; i++) asm volatile("" ::"v"(mloc_t[i]));
+#pragma unroll
+        for (int j = 0; j < kMine; j++) asm volatile("" ::"v"(sraw[j][0]), "v"(sraw[j][1]));
+        wait_vmcnt<0>();  // this wave's V slices
+        if (t0 + kRing >= ntiles && w == 0 && lane == 0) atomic_add_async(u_old, sg + 1, 1);
         lds_barrier();
         // Tile sums, rescales and value MFMAs in key order. The tile sums are read up front, and
         // each tile's weights and value operand one tile ahead of its MFMAs.
@@ -507,11 +509,10 @@ __device__ __forceinline__ void consumer(const AttnArgs &a, char *lds, int64_t u
     }
     // The last consumer of the group advances E for the next launch on this workspace (every
     // read of this launch's ready words is done by then).
-    if (w == 0 && lane == 0) {
-        const int hgs = n_hg - HPB * hb < HPB ? n_hg - HPB * hb : HPB;
-        const uint64_t nv = (uint64_t)hgs * kSplitSlices;
-        const uint64_t old = __hip_atomic_fetch_add(sg + 1, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (old == nv - 1) __hip_atomic_store(sg, e + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (w == 0) {
+        wait_vmcnt<0>();
+        register_ready(u_old);
+        if (lane == 0 && u_old == nv - 1) __hip_atomic_store(sg, e + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 

@@ -1,5 +1,6 @@
-"""The attention kernels load each unit's query and sinks with inline-asm loads whose
-destination registers fill in asynchronously: the compiler sees a finished value at the
+"""The attention kernels load each unit's query and sinks with inline-asm loads (and the split
+kernel's consumers add to their group's count with an inline-asm atomic) whose destination
+registers fill in asynchronously: the compiler sees a finished value at the
 load, so nothing stops it from copying or spilling those registers before the data has
 arrived. The kernels are correct only if it never does, i.e. if every instruction that
 touches such a destination comes after an `s_waitcnt vmcnt` (the explicit waits that cover
@@ -19,7 +20,7 @@ from sparse_attention_attn_amd import build as B
 HIPCC = B.HIPCC if os.path.exists(B.HIPCC) else shutil.which("hipcc")
 pytestmark = pytest.mark.skipif(HIPCC is None, reason="hipcc not found")
 
-LOAD = re.compile(r"^\s*global_load_dword(?:x2|x3|x4)?\s+([av](?:\[\d+:\d+\]|\d+)),")
+LOAD = re.compile(r"^\s*(?:global_load_dword(?:x2|x3|x4)?|global_atomic_\w+)\s+([av](?:\[\d+:\d+\]|\d+)),")
 RANGE = re.compile(r"\b([av])\[(\d+):(\d+)\]")
 SINGLE = re.compile(r"\b([av])(\d+)\b")
 
