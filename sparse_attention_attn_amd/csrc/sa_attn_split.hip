@@ -18,8 +18,9 @@
 //     the tile's 64 K rows once, and 2 HPB of them run the score MFMA chain exactly as the
 //     persistent kernel does (one key half and one 16-head group each; same K slot order and
 //     operand layout). The block's query goes through LDS once (one 1 KiB DMA per head). It
-//     stores each scoring wave's raw scores, in its lane layout, and each key half's tile
-//     maximum per head, then publishes the tile's ready word. A narrower block puts each score
+//     stores each scoring wave's scaled scores (log2 units, masked past the row's count: the
+//     persistent kernels' tile_scores), in its lane layout, and each key half's tile maximum
+//     per head, then publishes the tile's ready word. A narrower block puts each score
 //     chain on a SIMD of its own, and the launch takes the narrowest that still fits the chip in
 //     one round of workgroups (one row: 16 heads, 10.6 against 12.5 us for 64).
 //   * consumer of (row, 16-head group, 64-column slice): it loads the row's index list and
@@ -88,7 +89,7 @@ __device__ __forceinline__ uint64_t ready_word(uint64_t e, int t) {
 // transposing read sit in four consecutive slots, which then use four different chunks.
 __device__ __forceinline__ int vswz(int s) { return s & 7; }
 
-// Workspace after the sync words: score tiles [row][tile][head group][key half][lane][8] fp32,
+// Workspace after the sync words: scaled score tiles [row][tile][head group][key half][lane][8] fp32,
 // then tile maxima [row][tile][head group][key half][head] fp32.
 __device__ __forceinline__ size_t score_block(int64_t row, int tile, int hg, int ntiles_max, int n_hg) {
     return (((size_t)row * ntiles_max + tile) * n_hg + hg) * (kSTileB / 4);
@@ -213,18 +214,19 @@ __device__ __forceinline__ void producer(const AttnArgs &a, char *lds, int64_t b
             const SA_LDS char *krow = (const SA_LDS char *)k_lds + (32 * kh + l16) * kKStride + 16 * g;
             f32x4 sacc0, sacc1;
             score_chain(krow, qreg, sacc0, sacc1, [](int) {});
+            // The half tile's scaled scores and their maximum per head: tile_scores on the same
+            // operands as in the persistent kernels (the consumers take both instead of computing
+            // them).
+            float sk[8];
+            const float mt = tile_scores(sacc0, sacc1, tile * kTile + 32 * kh + 8 * g, n, (tile + 1) * kTile <= n,
+                                         a.scale * kLog2e, sk);
             const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
                 (void *)((float *)((char *)a.ws + kSyncBytes) + score_block(row, tile, hg, ntiles_max, n_hg)), 0,
                 kSTileB, kBufferFlags);
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, sacc0), rs, (kh * 64 + lane) * 32, 0,
-                                                   kStoreDevice);
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, sacc1), rs, (kh * 64 + lane) * 32 + 16, 0,
-                                                   kStoreDevice);
-            // The half tile's maximum per head: tile_scores on the same operands as in the
-            // persistent kernels (the consumers take it instead of computing it).
-            float s_unused[8];
-            const float mt = tile_scores(sacc0, sacc1, tile * kTile + 32 * kh + 8 * g, n, (tile + 1) * kTile <= n,
-                                         a.scale * kLog2e, s_unused);
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, (f32x4){sk[0], sk[1], sk[2], sk[3]}), rs,
+                                                   (kh * 64 + lane) * 32, 0, kStoreDevice);
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, (f32x4){sk[4], sk[5], sk[6], sk[7]}), rs,
+                                                   (kh * 64 + lane) * 32 + 16, 0, kStoreDevice);
             const __amdgpu_buffer_rsrc_t rm = __builtin_amdgcn_make_buffer_rsrc(
                 (void *)((char *)a.ws + maxima_offset(a.rows, ntiles_max, n_hg) +
                          (((size_t)row * ntiles_max + tile) * n_hg + hg) * kMTileB),
@@ -247,7 +249,7 @@ __device__ __forceinline__ void producer(const AttnArgs &a, char *lds, int64_t b
 // Consumer task u of the launch: (row, 16-head group, 64-column slice), slices fastest. Eight
 // waves, two per SIMD: wave w takes key half kh = w >> 2 and the 16 columns cs*64 + 16(w & 3)
 // .. +15 (one MFMA block). The four waves of a key half split a round's tiles for the
-// expensive part of the online softmax (scaled scores, weights), share the weights through
+// expensive part of the online softmax (the weights), share the weights through
 // LDS, and each runs the cheap sequential parts (reference scan, tile sums) itself.
 template <int HPB>
 __device__ __forceinline__ void consumer(const AttnArgs &a, char *lds, int64_t u, int ntiles_max, int n_hb, int n_hg,
@@ -298,7 +300,6 @@ __device__ __forceinline__ void consumer(const AttnArgs &a, char *lds, int64_t u
     HalfState st;
     f32x4 acc[1];
     half_start(st, acc, kh == 0, sink);
-    const float scale2 = a.scale * kLog2e;
 
     const float *sws = (const float *)((const char *)a.ws + kSyncBytes) + score_block(row, 0, hg, ntiles_max, n_hg);
     const float *mws = (const float *)((const char *)a.ws + maxima_offset(a.rows, ntiles_max, n_hg)) +
@@ -426,10 +427,9 @@ __device__ __forceinline__ void consumer(const AttnArgs &a, char *lds, int64_t u
 #pragma unroll
                 for (int q = 1; q < 4; q++)
                     if (4 * j + q < kRing && qv == q) ref = ref_t[4 * j + q < kRing ? 4 * j + q : 0];
-                const int t = t0 + i;
                 float sk[8];
-                (void)tile_scores(sraw[j][0], sraw[j][1], t * kTile + 32 * kh + 8 * g, n, (t + 1) * kTile <= n, scale2,
-                                  sk);
+#pragma unroll
+                for (int e = 0; e < 8; e++) sk[e] = e < 4 ? sraw[j][0][e] : sraw[j][1][e - 4];
                 bf16x8 ph, pl;
                 const float psum = tile_weights(sk, ref, ph, pl);
                 SA_LDS bf16x8 *pp = (SA_LDS bf16x8 *)lds_at<bf16x8>(s_base + i * kSTileB + (kh * 64 + lane) * 32);
