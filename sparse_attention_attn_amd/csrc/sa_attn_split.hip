@@ -25,7 +25,8 @@
 //     one round of workgroups (one row: 16 heads, 10.6 against 12.5 us for 64).
 //   * consumer of (row, 16-head group, 64-column slice): it loads the row's index list and
 //     gathers the V column slices of a round of up to ten tiles while the producers run, waits
-//     for the ready words of the row's tiles, loads their scores and maxima, then runs, per wave
+//     for the ready words of the row's tiles, loads the scaled scores of the tiles it weighs and
+//     every tile's maxima straight into registers, then runs, per wave
 //     (key half kh = w >> 2, 16-column part w & 3), the same online-softmax steps and value MFMAs
 //     on each tile in order (the four waves of a key half share the weights), and the same
 //     fixed-order fold of the two key halves (sa_attn_common.h).
