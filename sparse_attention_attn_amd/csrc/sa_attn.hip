@@ -355,13 +355,14 @@ attn_bf16_kernel(AttnArgs a, int n_hg, int64_t units) {
         // ---- scores of the wave's 32 keys for its 16 heads over the full head width.
         f32x4 sacc0, sacc1;
         {
-            // The tile's V rows go out in the score steps, one every two, in the matrix pipe's
-            // shadow (every wave finished the previous tile's values before the barrier).
+            // The tile's V rows go out in the score steps, in the matrix pipe's shadow (every
+            // wave finished the previous tile's values before the barrier): one every two of a
+            // 16-step block chain, one every four of the 32-step two-block chain.
             const __amdgpu_buffer_rsrc_t rv = rsrc_v(cur);
-            auto hook = [&](int kk) {
-                if (kk % 2 == 0) dma_v_row(rv, iv_cur, kk / 2);
-            };
             if constexpr (kShareScores) {
+                auto hook = [&](int kk) {
+                    if (kk % 2 == 0) dma_v_row(rv, iv_cur, kk / 2);
+                };
                 f32x4 *xs = xs_lds[(kh * HQ + hq) * 2];
                 if (sblock >= 0) {
                     f32x4 sb;
@@ -375,7 +376,9 @@ attn_bf16_kernel(AttnArgs a, int n_hg, int64_t units) {
                 sacc0 = xs[lane];
                 sacc1 = xs[64 + lane];
             } else {
-                score_chain(krow, qreg, sacc0, sacc1, hook);
+                score_chain(krow, qreg, sacc0, sacc1, [&](int i) {
+                    if (i % 4 == 0) dma_v_row(rv, iv_cur, i / 4);
+                });
             }
         }
 
@@ -581,23 +584,28 @@ attn_bf16_alias_kernel(AttnArgs a, int n_hg, int64_t units) {
         // ---- scores of the wave's 32 keys for its 16 heads over the full head width.
         f32x4 sacc0 = (f32x4){}, sacc1 = (f32x4){};
         if (!kShareScores) {
+            // Block 0's chain, then block 1's (each the same MFMAs on the same operands in the same
+            // order as interleaved), with the K operand read kAhead reads ahead of its MFMA.
             const uint32_t kb = tb + kbase;
-            bf16x8 k0 = *lds_at<bf16x8>(kb);
-            bf16x8 k1 = *lds_at<bf16x8>(kb + 16 * kRowBytes);
+            constexpr int kAhead = 2;
+            // Block 1's base: adding 16 rows changes no bit that the step's XOR touches.
+            const uint32_t kb1 = kb + 16 * kRowBytes;
+            auto kread = [&](int i) {
+                const int kk = i & 15;
+                return *lds_at<bf16x8>((i >> 4 ? kb1 : kb) ^ (64u * kk));
+            };
+            bf16x8 ring[kAhead + 1];
 #pragma unroll
-            for (int kk = 0; kk < 16; kk++) {
-                bf16x8 n0 = k0, n1 = k1;
-                if (kk + 1 < 16) {
-                    n0 = *lds_at<bf16x8>(kb ^ (64u * (kk + 1)));
-                    n1 = *lds_at<bf16x8>((kb ^ (64u * (kk + 1))) + 16 * kRowBytes);
-                }
-                sacc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qreg[kk], sacc0, 0, 0, 0);
-                sacc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qreg[kk], sacc1, 0, 0, 0);
-                // Rows 0..3 of T(j+1), one every four steps.
-                if (more && kk % 4 == 0) dma_t_row(rt, iv_next, buf ^ 1, kk / 4);
+            for (int i = 0; i < kAhead; i++) ring[i] = kread(i);
+#pragma unroll
+            for (int i = 0; i < 32; i++) {
+                if (i + kAhead < 32) ring[(i + kAhead) % (kAhead + 1)] = kread(i + kAhead);
+                const int kk = i & 15;
+                if (i < 16) sacc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ring[i % (kAhead + 1)], qreg[kk], sacc0, 0, 0, 0);
+                else sacc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ring[i % (kAhead + 1)], qreg[kk], sacc1, 0, 0, 0);
+                // Rows 0..3 of T(j+1), one every eight steps.
+                if (more && i % 8 == 0) dma_t_row(rt, iv_next, buf ^ 1, i / 8);
                 __builtin_amdgcn_sched_barrier(0);
-                k0 = n0;
-                k1 = n1;
             }
         } else {
             // One block of the head group's score tile per computing wave (block b's chain: the

@@ -234,28 +234,28 @@ __device__ __forceinline__ void q_ready(bf16x8 (&qreg)[16], float &sink) {
 
 // Score MFMA chain of one wave: S^T = K Q^T for the 32 keys of its half (two 16-slot blocks)
 // and its 16 heads, over the full head width (16 steps of 32 dimensions). krow: the lane's
-// LDS base in the K buffer (slot 32kh + l16, dims 8g + 0..7; stride kKStride). Between steps
-// the caller's hook issues gathers in the matrix pipe's shadow.
+// LDS base in the K buffer (slot 32kh + l16, dims 8g + 0..7; stride kKStride). Block 0's chain
+// of 16 MFMAs runs first, then block 1's (the same MFMAs on the same operands, in the same order
+// per block, as any interleaving of the two), each K operand read two reads ahead of its MFMA.
+// After each of the 32 steps the caller's hook (step index 0..31) issues gathers in the matrix
+// pipe's shadow.
 template <typename Hook>
 __device__ __forceinline__ void score_chain(const SA_LDS char *krow, const bf16x8 (&qreg)[16], f32x4 &sacc0,
                                             f32x4 &sacc1, Hook &&hook) {
+    constexpr int kAhead = 2;
     sacc0 = (f32x4){};
     sacc1 = (f32x4){};
-    bf16x8 k0 = *(const SA_LDS bf16x8 *)(krow);
-    bf16x8 k1 = *(const SA_LDS bf16x8 *)(krow + 16 * kKStride);
+    auto kread = [&](int i) { return *(const SA_LDS bf16x8 *)(krow + (i >> 4) * 16 * kKStride + 64 * (i & 15)); };
+    bf16x8 ring[kAhead + 1];
 #pragma unroll
-    for (int kk = 0; kk < 16; kk++) {
-        bf16x8 n0 = k0, n1 = k1;
-        if (kk + 1 < 16) {
-            n0 = *(const SA_LDS bf16x8 *)(krow + 64 * (kk + 1));
-            n1 = *(const SA_LDS bf16x8 *)(krow + 16 * kKStride + 64 * (kk + 1));
-        }
-        sacc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qreg[kk], sacc0, 0, 0, 0);
-        sacc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qreg[kk], sacc1, 0, 0, 0);
-        hook(kk);
+    for (int i = 0; i < kAhead; i++) ring[i] = kread(i);
+#pragma unroll
+    for (int i = 0; i < 32; i++) {
+        if (i + kAhead < 32) ring[(i + kAhead) % (kAhead + 1)] = kread(i + kAhead);
+        if (i < 16) sacc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ring[i % (kAhead + 1)], qreg[i], sacc0, 0, 0, 0);
+        else sacc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ring[i % (kAhead + 1)], qreg[i - 16], sacc1, 0, 0, 0);
+        hook(i);
         __builtin_amdgcn_sched_barrier(0);
-        k0 = n0;
-        k1 = n1;
     }
 }
 
