@@ -206,6 +206,23 @@ def copy_peak(torch, dev, mib: int = 1024, reps: int = 10):
     return {"gbs": 2 * n / (ms * 1e-3) / 1e9, "bytes_moved_per_copy": 2 * n, "kernel_ms": ms}
 
 
+def decode_kernel_label(torch, sa, dev, rows: int, heads: int, k: int, n_ctx: int, alias: bool) -> str:
+    """Name of the kernel a bf16 decode launch of this shape runs, as the library's launch plan
+    picks it (sa_attn.hip, plan_attn_bf16): the split path when the call needs a workspace, else
+    the persistent kernel with 16 x HQ heads per workgroup and NS column slices."""
+    if sa.workspace_bytes(0, rows, heads, k, n_ctx) > 0:
+        return "attn_split_kernel (sparse_attn_decode, split path)"
+    hq = 4 if heads > 32 else (2 if heads > 16 else 1)
+    rows_hg = rows * -(-heads // (16 * hq))
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    ns = 1
+    while ns < 2 * hq and rows_hg * 2 * ns <= cus:
+        ns *= 2
+    if alias:
+        return f"attn_bf16_alias_kernel<{hq},{ns}> (sparse_attn_decode, K = V)"
+    return f"attn_bf16_kernel<{hq},{ns}> (sparse_attn_decode)"
+
+
 def small_batch_latency(torch, sa, w, dev, n_ctx: int, k: int, heads: int, seed: int):
     """Attention call latency at 1 and 8 sequences (the split path): the median over 32 warm
     calls, each bracketed by HIP events on the launch stream with the device idle before it (a
@@ -490,7 +507,7 @@ def main() -> int:
 
     inp, scores, idx, cnt, out = sets[(args.steps - 1) % 2]  # the last timed step's set
     result = {
-        "metric": "decode query-rows*heads/s (64 heads, d=512, k=640)",
+        "metric": f"decode query-rows*heads/s ({H} heads, d=512, k={K})",
         "value": B * H / (ms_per_step * 1e-3),
         "unit": "query-rows*heads/s",
         "n_gpus": 1,
@@ -517,8 +534,7 @@ def main() -> int:
             "unit": "GB/s",
             "frac": achieved_gbs / HBM_PEAK_GBS,
             "traffic": None if alias else measured_traffic(B, H, N, K),
-            "kernel": "attn_bf16_alias_kernel<4,1> (sparse_attn_decode, K = V)" if alias
-                      else "attn_bf16_kernel<4,1> (sparse_attn_decode)",
+            "kernel": decode_kernel_label(torch, sa, dev, B, H, K, N, alias),
             "kernel_ms": attn_ms,
             "algorithmic_bytes_per_launch": nbytes,
             "mfma_tflops": flops / (attn_ms * 1e-3) / 1e12,

@@ -32,3 +32,32 @@ def test_code_hash_sees_code_changes_and_file_order(tmp_path):
 def test_traffic_only_for_the_recorded_workload():
     assert bench.measured_traffic(8, 64, 32768, 640) is None
     assert bench.measured_traffic(1024, 16, 4096, 640) is None
+
+
+class _StubSA:
+    """workspace_bytes as the library plans it: the split path below 24 (row, 64-head block)
+    pairs with at most 1,024 indices per row."""
+    @staticmethod
+    def workspace_bytes(op, rows, heads, k, n_ctx):
+        return 1 if k <= 1024 and rows * -(-heads // 64) < 24 else 0
+
+
+class _StubTorch:
+    class cuda:
+        @staticmethod
+        def get_device_properties(dev):
+            class P:
+                multi_processor_count = 256
+            return P()
+
+
+def test_decode_kernel_label_follows_the_launch_plan():
+    lab = lambda rows, heads, alias=False: bench.decode_kernel_label(_StubTorch, _StubSA, None, rows, heads, 640,
+                                                                   4096, alias)
+    assert lab(1024, 64) == "attn_bf16_kernel<4,1> (sparse_attn_decode)"
+    assert lab(1024, 64, True) == "attn_bf16_alias_kernel<4,1> (sparse_attn_decode, K = V)"
+    assert lab(1024, 32) == "attn_bf16_kernel<2,1> (sparse_attn_decode)"
+    assert lab(1024, 16) == "attn_bf16_kernel<1,1> (sparse_attn_decode)"
+    assert lab(64, 64) == "attn_bf16_kernel<4,4> (sparse_attn_decode)"
+    assert lab(24, 64) == "attn_bf16_kernel<4,8> (sparse_attn_decode)"
+    assert lab(8, 64).startswith("attn_split_kernel")
