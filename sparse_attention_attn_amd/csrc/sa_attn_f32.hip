@@ -189,19 +189,20 @@ attn_f32_kernel(AttnArgs a, int n_hg) {
         l = f32_l_step(alpha, l, psum);
         m = m_new;
         ref = ref_new;
-#pragma unroll
-        for (int cb = 0; cb < 4; cb++) acc[cb] *= alpha;
         // ---- values: V(t) has landed (after it only K(t+1) is in flight)
         if (more) wait_vmcnt<8>(); else wait_vmcnt<0>();
         lds_barrier();
+        f32x4 tv[4] = {};
 #pragma unroll
         for (int st = 0; st < 8; st++) {
 #pragma unroll
             for (int cb = 0; cb < 4; cb++) {
                 const float vx = *(const SA_LDS float *)(vrow + 4 * st * kVStrF + 64 * cb);
-                acc[cb] = __builtin_amdgcn_mfma_f32_16x16x4f32(vx, pe[st], acc[cb], 0, 0, 0);
+                tv[cb] = __builtin_amdgcn_mfma_f32_16x16x4f32(vx, pe[st], tv[cb], 0, 0, 0);
             }
         }
+#pragma unroll
+        for (int cb = 0; cb < 4; cb++) acc[cb] = f32_acc_step(acc[cb], alpha, tv[cb]);
         iv_cur = iv_next;
     }
     wait_vmcnt<0>();

@@ -8,7 +8,8 @@
 // maximum, a tile sum and a value sum; TensorFold pull request 1206, "What changes": a sink
 // logit per head. Float32 throughout (the weights are never rounded to a narrower type). Per
 // 32-key tile: m' = max(m, tile maximum), reference r = m' (0 while m' = -inf), alpha =
-// exp(m - r), p = exp(s - r) (0 for a masked key), l = alpha l + sum p, acc = alpha acc + P V.
+// exp(m - r), p = exp(s - r) (0 for a masked key), l = alpha l + sum p, acc = alpha acc + P V
+// (the tile's P V summed on its own first).
 // Contraction is off here: a product followed by a sum is never fused, in any caller.
 #pragma once
 
@@ -70,6 +71,15 @@ __device__ __forceinline__ float f32_tile_weights(const float (&s)[8], float ref
 __device__ __forceinline__ float f32_l_step(float alpha, float l, float psum) {
 #pragma clang fp contract(off)
     return alpha * l + psum;
+}
+
+// Value sum step: the tile's P V (its own MFMA chain, started from zero) added once to the
+// rescaled running sum, a product then a sum. The running sum thus takes one rounding per
+// tile, not one per MFMA step of four keys: with many equal weights (a short cache, duplicate
+// indices), per-step roundings at the running sum's magnitude add up past 1e-5.
+__device__ __forceinline__ f32x4 f32_acc_step(const f32x4 &acc, float alpha, const f32x4 &tile) {
+#pragma clang fp contract(off)
+    return acc * alpha + tile;
 }
 
 }  // namespace sa

@@ -360,10 +360,11 @@ attn_f32_split_values_kernel(AttnArgs a, int ntiles_max, int n_hg) {
                 for (int st = 0; st < 8; st++) vx_n[st] = vx_c[st];
                 if (i + 1 < kRingF) operands(i + 1, pa_n, pb_n, vx_n);
                 l = f32_l_step(alpha_t[i], l, psum_t[i]);
-                acc *= alpha_t[i];
                 const float pe[8] = {pa_c[0], pa_c[1], pa_c[2], pa_c[3], pb_c[0], pb_c[1], pb_c[2], pb_c[3]};
+                f32x4 tv = {};
 #pragma unroll
-                for (int st = 0; st < 8; st++) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(vx_c[st], pe[st], acc, 0, 0, 0);
+                for (int st = 0; st < 8; st++) tv = __builtin_amdgcn_mfma_f32_16x16x4f32(vx_c[st], pe[st], tv, 0, 0, 0);
+                acc = f32_acc_step(acc, alpha_t[i], tv);
                 // Slot i has been read (its values are in vx_c, used above): refill it.
                 if (t1 + i < ntiles) issue_v(t1 + i, i);
                 pa_c = pa_n;

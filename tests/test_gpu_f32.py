@@ -102,3 +102,22 @@ def test_repeats_are_identical():
     torch.cuda.synchronize()
     for o in outs[1:]:
         assert torch.equal(o.view(torch.int32), outs[0].view(torch.int32))
+
+
+@pytest.mark.parametrize("rows,heads,n_ctx,kmax", [(18, 65, 1, 452), (4, 16, 5, 788), (3, 64, 2, 1000), (20, 64, 3, 640)])
+def test_heavily_duplicated_selections(rows, heads, n_ctx, kmax):
+    """Hundreds of entries drawn from a cache of one to five positions (duplicates are summed):
+    many equal weights, so the value sum's rounding must not grow with the number of entries.
+    Both float32 paths: the split path (4 rows of 16 heads, 3 rows of 64) and attn_f32_kernel."""
+    rng = np.random.default_rng(600 + n_ctx)
+    q = w._normal(rng, (rows, heads, w.D))
+    k = w._normal(rng, (rows, n_ctx, w.D))
+    v = w._normal(rng, (rows, n_ctx, w.D))
+    sinks = rng.standard_normal(heads).astype(np.float32)
+    idx = rng.integers(0, n_ctx, size=(rows, kmax)).astype(np.int32)
+    nsel = np.full(rows, kmax, dtype=np.int32)
+    nsel[-1] = kmax // 2 + 1
+    idx[-1, nsel[-1]:] = -1
+    case = w.AttnCase(f"f32 duplicates R={rows} H={heads} N={n_ctx} kmax={kmax}", "f32", q, k, v, idx, nsel, sinks,
+                      w.SCALE, False)
+    check(case)
