@@ -253,6 +253,57 @@ def test_largest_cache(alias):
     say(f"  ok {st}")
 
 
+@pytest.mark.parametrize("dtype,rows,alias", [("bf16", 32, False), ("bf16", 32, True), ("f32", 32, False),
+                                               ("f32", 4, False)])
+def test_largest_shared_cache_with_masked_entries(dtype, rows, alias):
+    """One shared cache of the largest size each storage type allows (2^22 - 1 bf16 positions,
+    2^21 - 1 float32 positions: 4 GiB per tensor), read by a prefill launch that takes the
+    persistent kernels (bf16, 32 rows; attn_f32_kernel, 32 rows) or the float32 split path
+    (4 rows). Every row holds masked entries (-1) past a count below kmax, whose wrapped byte
+    offsets sit at the 32-bit buffer range's end, next to selected positions at both ends of the
+    cache (0, 1, 2^21 or 2^20, N - 2, N - 1). The oracle evaluates the same selections on a
+    compact cache of the 640 positions used."""
+    import sparse_attention_attn_amd as sa
+    from sparse_attention_attn_amd import _lib
+    N = _lib.SA_BF16_MAX_CTX if dtype == "bf16" else _lib.SA_F32_MAX_CTX
+    rng = np.random.default_rng(97 + rows)
+    kmax = 640
+    normal = w._normal_bf16 if dtype == "bf16" else w._normal
+    q = normal(rng, (rows, 64, w.D))
+    kc = normal(rng, (1, kmax, w.D))
+    vc = kc if alias else normal(rng, (1, kmax, w.D))
+    sinks = rng.standard_normal(64).astype(np.float32)
+    idx = np.empty((rows, kmax), dtype=np.int32)
+    nsel = rng.integers(kmax // 2, kmax, size=rows).astype(np.int32)  # below kmax: masked tails
+    for r in range(rows):
+        idx[r, : nsel[r]] = rng.permutation(kmax)[: nsel[r]]
+        idx[r, nsel[r]:] = -1
+    small = w.AttnCase(f"largest shared cache {dtype}", dtype, q, kc, vc, idx, nsel, sinks, w.SCALE, True)
+    # compact position i of the oracle's cache lives at big position pos[i]
+    fixed = np.array([0, 1, (N + 1) // 2, N - 2, N - 1], dtype=np.int64)
+    others = rng.choice(np.arange(2, N - 2, dtype=np.int64), size=kmax - len(fixed), replace=False)
+    pos = np.sort(np.concatenate([fixed, others]))
+    assert len(np.unique(pos)) == kmax
+    say(f"largest shared cache N={N} {dtype}{' aliased' if alias else ''}: {rows} rows x {kmax}, 64 heads")
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    d = to_device(small, DEV)
+    kd = torch.zeros((N, w.D), dtype=tdt, device=DEV)
+    vd = kd if alias else torch.zeros((N, w.D), dtype=tdt, device=DEV)
+    pos_d = torch.from_numpy(pos).to(DEV)
+    kd[pos_d] = d["k"]
+    if not alias:
+        vd[pos_d] = d["v"]
+    big = np.where(idx >= 0, pos[np.maximum(idx, 0)], -1).astype(np.int32)
+    got = sa.prefill(d["q"], kd, vd, torch.from_numpy(big).to(DEV), d["sinks"], small.scale, d["nsel"]).cpu().numpy()
+    torch.cuda.synchronize()
+    del kd, vd
+    torch.cuda.empty_cache()
+    sel = sorted({0, rows // 2, rows - 1})
+    ref = run_oracle(small, rows=sel)
+    st = assert_parity(got[sel], ref[sel], *(BF16_TOL if dtype == "bf16" else F32_TOL), small.name)
+    say(f"  ok {st}")
+
+
 def test_determinism_and_guards():
     """Five repeats are byte-identical and never write outside their output."""
     import sparse_attention_attn_amd as sa
