@@ -64,23 +64,25 @@ __global__ void __launch_bounds__(kThreads) topk_radix_kernel(TopkArgs a) {
     const int k = a.k;
 
     if (vl <= k) {  // every candidate is selected
-        for (int i = t; i < k; i += kThreads) orow[i] = i < vl ? i : -1;
+        for (int64_t i = t; i < k; i += kThreads) orow[i] = i < vl ? (int32_t)i : -1;
         if (t == 0 && a.count_out) a.count_out[row] = vl;
         return;
     }
 
     const bool in_lds = vl <= kLdsKeys;
     if (in_lds) {
-        for (int i = t; i < vl; i += kThreads) keys[i] = order_key(srow[i]);
+        for (int i = t; i < vl; i += kThreads) keys[i] = order_key(srow[i]);  // vl <= kLdsKeys here
     }
-    auto key_at = [&](int i) -> uint32_t { return in_lds ? keys[i] : order_key(srow[i]); };
+    // Loop counters over a row are 64-bit: a row may hold up to 2^31 - 1 scores, and a 32-bit
+    // counter stepping past its end would overflow.
+    auto key_at = [&](int64_t i) -> uint32_t { return in_lds ? keys[i] : order_key(srow[i]); };
 
     // ---- radix select of the k-th largest key.
     uint32_t prefix = 0u, mask = 0u, krem = (uint32_t)k;
     for (int shift = 24; shift >= 0; shift -= 8) {
         if (t < 256) hist[t] = 0u;
         __syncthreads();
-        for (int i = t; i < vl; i += kThreads) {
+        for (int64_t i = t; i < vl; i += kThreads) {
             const uint32_t u = key_at(i);
             if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1u);
         }
@@ -118,8 +120,8 @@ __global__ void __launch_bounds__(kThreads) topk_radix_kernel(TopkArgs a) {
 
     // ---- ordered compaction.
     uint32_t base_eq = 0u, base_sel = 0u;
-    for (int b0 = 0; b0 < vl; b0 += kThreads) {
-        const int i = b0 + t;
+    for (int64_t b0 = 0; b0 < vl; b0 += kThreads) {
+        const int64_t i = b0 + t;
         const uint32_t u = i < vl ? key_at(i) : 0u;
         const bool gt = i < vl && u > T;
         const bool eq = i < vl && u == T;
@@ -146,7 +148,7 @@ __global__ void __launch_bounds__(kThreads) topk_radix_kernel(TopkArgs a) {
             sel_total += c;
         }
         const uint32_t pos = base_sel + sel_before + lanes_below(msel);
-        if (sel && pos < (uint32_t)k) orow[pos] = i;  // exactly k are selected; the bound is a guard
+        if (sel && pos < (uint32_t)k) orow[pos] = (int32_t)i;  // exactly k are selected; the bound is a guard
         base_eq += eq_total;
         base_sel += sel_total;
         __syncthreads();
@@ -204,7 +206,7 @@ __device__ __forceinline__ void topk_regs_row(TopkArgs a) {
     const uint32_t k = (uint32_t)a.k;
 
     if ((uint32_t)vl <= k) {  // every candidate is selected
-        for (int i = threadIdx.x; i < a.k; i += 64 * WAVES) orow[i] = i < vl ? i : -1;
+        for (int64_t i = threadIdx.x; i < a.k; i += 64 * WAVES) orow[i] = i < vl ? (int32_t)i : -1;
         if (threadIdx.x == 0 && a.count_out) a.count_out[row] = vl;
         return;
     }
