@@ -456,17 +456,18 @@ def main() -> int:
     # The gather ceiling: the same index-driven K and V row gathers with no compute
     # (sparse_attn_gather_probe), timed live over the same two input sets and their top-k index
     # lists, with 8 and 16 rows in flight per wave; the faster one is the ceiling the attention
-    # kernel is compared with. It runs before the warm-up steps with a fixed number of launches
-    # (about 100 ms of gathers), so the part's clocks have ramped up under this load whatever the
-    # warm-up count.
+    # kernel is compared with. It runs right before the warm-up steps with a fixed number of
+    # launches (about 100 ms of gathers), after the plain copy measured as context: attention
+    # launches that follow the gathers settle sooner than ones that follow the copy.
     ceiling = None
     if not alias:
+        cpeak = copy_peak(torch, dev)
         for st in sets:
             if not args.attn_only:
                 sa.topk(st[1], K, idx_out=st[2], count_out=st[3])
         ceiling = gather_ceiling(torch, sa, [(st[0], st[2] if not args.attn_only else st[0]["idx"]) for st in sets],
                                  B, K, reps=250)
-        ceiling["copy_peak"] = copy_peak(torch, dev)
+        ceiling["copy_peak"] = cpeak
 
     for i in range(args.warmup):
         step(i)
