@@ -57,8 +57,12 @@ attn_f32_kernel(AttnArgs a, int n_hg) {
     const int l16 = lane & 15;
     const int b_own = w & 1;
     const int dq = w >> 1;
-    const int64_t row = blockIdx.x / n_hg;
-    const int hg = (int)(blockIdx.x % n_hg);
+    // XCD-aware order (each XCD takes every eighth workgroup id; xcd_remap gives it a contiguous
+    // range of units): the head groups of one row run on one XCD, so that their gathers of the
+    // same cache rows share that XCD's L2 instead of each fetching them from beyond it.
+    const int64_t u = xcd_remap(blockIdx.x, gridDim.x);
+    const int64_t row = u / n_hg;
+    const int hg = (int)(u % n_hg);
     const int head = 16 * hg + l16;
     const bool head_ok = head < a.H;
 

@@ -87,7 +87,9 @@ attn_f32_split_scores_kernel(AttnArgs a, int ntiles_max, int n_hb, int n_hg) {
     constexpr int NB = HPB == 1 ? 1 : 2;
     const int half = w & 1;
     const int dq = w >> 1;
-    const int64_t bid = blockIdx.x;
+    // XCD-aware order: the head blocks of one tile run on one XCD, where their gathers of the
+    // same K rows share its L2.
+    const int64_t bid = xcd_remap(blockIdx.x, gridDim.x);
     const int hb = (int)(bid % n_hb);
     const int tile = (int)((bid / n_hb) % ntiles_max);
     const int64_t row = bid / ((int64_t)n_hb * ntiles_max);
