@@ -276,6 +276,16 @@ def small_batch_latency(torch, sa, w, dev, n_ctx: int, k: int, heads: int, seed:
 MFMA_F32_PEAK_TFLOPS = 157.3
 
 
+def f32_kernel_label(rows, heads, k):
+    """The float32 attention kernels of a decode launch, as the library picks them
+    (f32_split_applies in csrc/sa_attn_f32_split.hip): the split path for fewer than 24
+    (row, 64-head block) pairs and 129 <= k <= 1,024, else attn_f32_kernel. Both give the same bits."""
+    n_hb = (heads + 63) // 64
+    if 128 < k <= 1024 and rows * n_hb < 24:
+        return "attn_f32_split_scores_kernel + attn_f32_split_values_kernel (sparse_attn_decode, SA_F32, split path)"
+    return "attn_f32_kernel (sparse_attn_decode, SA_F32)"
+
+
 def bench_decode_f32(args, torch, sa, w, dev) -> int:
     """Float32 decode step, batched-decode shape (8 sequences x 32,768 positions unless --batch /
     --n-ctx say otherwise): top-k over each row's scores, then float32 attention on the matrix
@@ -340,7 +350,7 @@ def bench_decode_f32(args, torch, sa, w, dev) -> int:
                    "batch_rows": B, "heads": H, "head_dim": D, "n_ctx": N, "k": K},
         "roofline": {"bound": "mfma", "achieved": tflops, "peak": MFMA_F32_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": tflops / MFMA_F32_PEAK_TFLOPS, "traffic": None,
-                     "kernel": "attn_f32_kernel (sparse_attn_decode, SA_F32)", "kernel_ms": attn_ms,
+                     "kernel": f32_kernel_label(B, H, K), "kernel_ms": attn_ms,
                      "algorithmic_flops_per_launch": flops, "algorithmic_bytes_per_launch": nbytes,
                      "hbm_gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS},
         "cpu_baseline": None,

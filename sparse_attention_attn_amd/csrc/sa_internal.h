@@ -77,11 +77,12 @@ hipError_t launch_attn_split(const AttnArgs &a, hipStream_t s);
 // kF32SplitMaxUnits (row, 64-head block) pairs and index lists of more than kF32SplitMinK (and
 // at most kSplitMaxK) entries, a subset of the bf16 split's launches, so that
 // sparse_attn_workspace_bytes, which has no dtype, stays an upper bound. Measured on 64 heads at
-// k = 640: 23 us at 1 row, 35 at 8 and 64 at 16 against about 83 us for attn_f32_kernel; at 23
-// rows its values kernel would run three waves of workgroups. Index lists of at most four tiles
-// are as fast in attn_f32_kernel. The score tiles take rows x ceil(kmax / 32) x ceil(H / 16) x
+// k = 640 over 4,096 positions: 22 us at 1 row, 57 at 16 and 75-77 at 17-23 rows, against about
+// 86 us for attn_f32_kernel at 17-23 rows (each workgroup a chain of twenty 32-key tiles), so the
+// float32 split takes every launch the bf16 split takes. Index lists of at most four tiles are
+// as fast in attn_f32_kernel. The score tiles take rows x ceil(kmax / 32) x ceil(H / 16) x
 // 2 KiB of workspace, never more than the bf16 split's. Both float32 paths give the same bits.
-constexpr int64_t kF32SplitMaxUnits = 17;
+constexpr int64_t kF32SplitMaxUnits = 24;
 constexpr int32_t kF32SplitMinK = 128;
 static_assert(kF32SplitMaxUnits <= kSplitMaxUnits, "the float32 split's launches are the bf16 split's");
 bool f32_split_applies(int64_t rows, int H, int32_t kmax);

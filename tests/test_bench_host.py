@@ -61,3 +61,17 @@ def test_decode_kernel_label_follows_the_launch_plan():
     assert lab(64, 64) == "attn_bf16_kernel<4,4> (sparse_attn_decode)"
     assert lab(24, 64) == "attn_bf16_kernel<4,8> (sparse_attn_decode)"
     assert lab(8, 64).startswith("attn_split_kernel")
+
+
+def test_f32_kernel_label_follows_the_launch_rule():
+    """The float32 bench line names the kernels the library launches: the split path below 24
+    (row, 64-head block) pairs with 129 <= k <= 1,024, attn_f32_kernel otherwise."""
+    split = "attn_f32_split_scores_kernel"
+    assert bench.f32_kernel_label(8, 64, 640).startswith(split)
+    assert bench.f32_kernel_label(23, 64, 640).startswith(split)
+    assert bench.f32_kernel_label(24, 64, 640).startswith("attn_f32_kernel")
+    assert bench.f32_kernel_label(64, 64, 640).startswith("attn_f32_kernel")
+    assert bench.f32_kernel_label(8, 64, 128).startswith("attn_f32_kernel")
+    assert bench.f32_kernel_label(8, 64, 1025).startswith("attn_f32_kernel")
+    assert bench.f32_kernel_label(11, 128, 640).startswith(split)
+    assert bench.f32_kernel_label(12, 128, 640).startswith("attn_f32_kernel")
